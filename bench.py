@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed-ternary x q8_K hot path on one MI355X.
+
+One step = one pass of the decode hot path over one token: q8_K quantization
+of a fresh fp32 activation vector, then the 32768 x 8192 pq2_0 matrix-vector
+product (tq_quantize_q8k + tq_gemv through the C ABI).  The weights are
+resident in HBM; eight repacked copies (570 MB) are rotated so that the
+256 MB Infinity Cache cannot serve a repeat call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  `value` is Gweights/s of the whole timed region (K
+steps captured in one HIP graph and replayed once, bracketed by
+synchronizations).  `roofline` is the matrix-vector kernel's algorithmic HBM
+bytes per launch divided by its mean duration, measured with HIP events
+around every launch of a second, eager pass of K steps on the same stream.
+`extra` carries the prompt-product (17408 x 5120, 4 and 64 tokens) and
+ptq1_0 figures; `cpu_baseline` times the CPU oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tq_inputs as TI  # noqa: E402
+
+METRIC = "Gweights/s + % peak HBM GB/s, ternary GEMV 32768×8192; GMAC/s prefill 64 tok"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS = 2 x MAC/s)
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-extra", action="store_true", help="skip the prompt-product and ptq1_0 figures")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="wall budget of the CPU baseline")
+    return ap.parse_args()
+
+
+def copies_for(nbytes: int) -> int:
+    """Enough distinct weight copies that the rotation exceeds twice the MALL."""
+    return max(2, -(-2 * MALL_BYTES // nbytes))
+
+
+class Timed:
+    """Per-launch HIP events on the current stream."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.i = 0
+
+    def around(self, fn):
+        a, b = self.ev[self.i]
+        a.record()
+        fn()
+        b.record()
+        self.i += 1
+
+    def mean_us(self):
+        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.ev[: self.i]]))
+
+
+def graph_time(torch, step, K):
+    """Capture K calls of step() in one graph, replay once; returns seconds."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)  # one eager call on the capture stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def decode_bench(torch, tq, K, W):
+    fmt, Wc, x = TI.make("decode_32768x8192")
+    R, G, _ = Wc.shape
+    C = G * 128
+    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
+    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
+    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
+    del wdev
+    # a fresh activation vector per step: rotate over a pool of distinct vectors
+    xs = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 1), 64, C)).cuda()
+    q = torch.empty((1, C), dtype=torch.int8, device="cuda")
+    d = torch.empty((1, C // 256), dtype=torch.float32, device="cuda")
+    bs = torch.empty((1, C // 16), dtype=torch.int16, device="cuda")
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+
+    def step(i, timer=None):
+        tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs))
+        call = lambda: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+        call() if timer is None else timer.around(call)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    # eager pass with per-launch events (roofline of the matrix-vector kernel)
+    timer = Timed(torch, K)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, timer)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    gemv_us = timer.mean_us()
+    # graph pass: the timed region of `value`
+    graph_s = graph_time(torch, step, K)
+    algo_bytes = tq.repacked_bytes(fmt, R, C) + C + 4 * (C // 256) + 4 * R
+    return {
+        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "eager_s": eager_s, "gemv_us": gemv_us,
+        "algo_bytes": algo_bytes, "weight_bytes": tq.repacked_bytes(fmt, R, C),
+    }
+
+
+def prefill_bench(torch, tq, T, K):
+    fmt, Wc, x = TI.make("prefill_17408x5120_t64" if T == 64 else "prefill_17408x5120_t4")
+    R, G, _ = Wc.shape
+    C = G * 128
+    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
+    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
+    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
+    del wdev
+    q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+    y = torch.empty((T, R), dtype=torch.float32, device="cuda")
+    call = lambda i: tq.gemm(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+    for i in range(20):
+        call(i)
+    torch.cuda.synchronize()
+    timer = Timed(torch, K)
+    for i in range(K):
+        timer.around(lambda: call(i))
+    torch.cuda.synchronize()
+    us = timer.mean_us()
+    macs = R * C * T
+    return {"tokens": T, "us": us, "gmac_s": macs / us / 1e3, "mfma_frac": 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12),
+            "hbm_gbs": (tq.repacked_bytes(fmt, R, C) + T * C + 4 * T * (C // 256) + 4 * T * R) / us / 1e3}
+
+
+def ptq1_bench(torch, tq, K):
+    fmt, Wc, x = TI.make("ptq1_32768x8192")
+    R, G, _ = Wc.shape
+    C = G * 128
+    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
+    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
+    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
+    del wdev
+    q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+    call = lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+    for i in range(20):
+        call(i)
+    torch.cuda.synchronize()
+    timer = Timed(torch, K)
+    for i in range(K):
+        timer.around(lambda: call(i))
+    torch.cuda.synchronize()
+    us = timer.mean_us()
+    wb = tq.repacked_bytes(fmt, R, C)
+    return {"us": us, "gweights_s": R * C / us / 1e3, "weight_gbs": wb / us / 1e3, "hbm_frac": wb / us / 1e3 / HBM_PEAK_GBS}
+
+
+def quantize_bench(torch, tq, K):
+    C = 8192
+    xs = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 2), 1, C)).cuda()
+    out = (torch.empty((1, C), dtype=torch.int8, device="cuda"), torch.empty((1, 32), dtype=torch.float32, device="cuda"),
+           torch.empty((1, 512), dtype=torch.int16, device="cuda"))
+    for _ in range(20):
+        tq.quantize_q8k(xs, out=out)
+    timer = Timed(torch, K)
+    for _ in range(K):
+        timer.around(lambda: tq.quantize_q8k(xs, out=out))
+    torch.cuda.synchronize()
+    return {"cols": C, "us": timer.mean_us()}
+
+
+def ceiling_probe(torch):
+    """Plain streaming kernels of known size: torch's sum (read) and copy."""
+    n = (2 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        a.sum()
+        b.copy_(a[: n // 2])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 10 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    e0.record()
+    for _ in range(10):
+        b.copy_(a[: n // 2])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * 4 * (n // 2) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return {"read_sum_2GiB_gbs": read_gbs, "copy_1GiB_gbs": copy_gbs}
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle on the host cores: quantize + product over the full
+    32768 x 8192 matrix, repeated while the wall budget lasts."""
+    import oracle
+
+    oracle.build(force=False)
+    fmt, Wc, x = TI.make("decode_32768x8192")
+    R, G, _ = Wc.shape
+    cores = len(os.sched_getaffinity(0))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        q, d, _ = oracle.quantize_q8k(x)
+        oracle.matmul(fmt, Wc, q, d, threads=cores)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": passes * R * G * 128 / dt / 1e9, "unit": "Gweights/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} full passes (q8_K quantize + 32768x8192 pq2_0 product, fp64 epilogue) over {dt:.1f} s, "
+                      f"row ranges split over {cores} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import bit_quantized_matvec_amd as tq
+
+    log("decode bench")
+    dec = decode_bench(torch, tq, args.steps, args.warmup)
+    R, C, K = dec["R"], dec["C"], args.steps
+    value = K * R * C / dec["graph_s"] / 1e9
+    achieved = dec["algo_bytes"] / (dec["gemv_us"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["graph_s"] * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode_32768x8192", "format": "pq2_0", "rows": R, "cols": C, "tokens": 1,
+                   "step": "tq_quantize_q8k + tq_gemv", "weight_copies_rotated": dec["copies"], "timing": "hip graph of K steps"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_pq2_kernel", "kernel_us": round(dec["gemv_us"], 3), "algo_bytes": dec["algo_bytes"]},
+    }
+    extra = {"decode_eager_gweights_s": round(K * R * C / dec["eager_s"] / 1e9, 2),
+             "decode_weight_gbs": round(dec["weight_bytes"] / (dec["gemv_us"] * 1e-6) / 1e9, 1),
+             "decode_gemv_gweights_s": round(R * C / dec["gemv_us"] / 1e3, 1)}
+    if not args.no_extra:
+        log("prefill / ptq1 / quantize / ceiling")
+        for T in (4, 64):
+            p = prefill_bench(torch, tq, T, 200)
+            extra[f"prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
+        p = ptq1_bench(torch, tq, 200)
+        extra["ptq1_decode"] = {k: round(v, 4) for k, v in p.items()}
+        extra["quantize_8192"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in quantize_bench(torch, tq, 200).items()}
+        extra["ceiling"] = {k: round(v, 1) for k, v in ceiling_probe(torch).items()}
+    out["extra"] = extra
+    if not args.no_cpu:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

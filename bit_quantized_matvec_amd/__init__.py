@@ -1,0 +1,189 @@
+"""Python binding of libtq: packed-ternary weights x q8_K activations on MI355X.
+
+Argument marshalling only.  Every step of the path (repack, q8_K quantization,
+matrix-vector and small-batch matrix products) runs in the HIP kernels of
+``libtq.so`` behind the C ABI declared in ``include/tq.h``; PyTorch provides
+device memory and the current stream.  There is no CPU fallback: if the
+library is not built, importing this package fails.
+
+    import bit_quantized_matvec_amd as tq
+    W = tq.repack(w_canonical_cuda, "pq2_0", rows, cols)
+    q, d, bs = tq.quantize_q8k(x_cuda)          # x: float32 [tokens, cols]
+    y = tq.gemv("pq2_0", W, rows, cols, q, d, bs)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # load torch's HIP runtime first: libtq binds to the same libamdhip64
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_matvec_amd.build` first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_SIGS = {
+    "tq_check_shape": ([_i32, _i64, _i64, _i64], _i32),
+    "tq_canonical_bytes": ([_i32, _i64, _i64], _i64),
+    "tq_repacked_bytes": ([_i32, _i64, _i64], _i64),
+    "tq_repack": ([_i32, _p, _p, _i64, _i64, _p, _p], _i32),
+    "tq_unrepack": ([_i32, _p, _p, _i64, _i64, _p], _i32),
+    "tq_quantize_q8k": ([_p, _i64, _i64, _p, _p, _p, _p], _i32),
+    "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p], _i32),
+    "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p], _i32),
+    "tq_group_dots": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p], _i32),
+    "tq_status_str": ([_i32], ctypes.c_char_p),
+    "tq_last_hip_error": ([], _i32),
+    "tq_version": ([], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTS = tuple(_SIGS)
+FORMATS = {"pq2_0": 1, "ptq1_0": 2}
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.tq_status_str(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {_lib.tq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (ctypes), for callers that want the raw ABI."""
+    return _lib
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise TQError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}")
+
+
+def check_shape(fmt, rows: int, cols: int, tokens: int = 1) -> int:
+    return _lib.tq_check_shape(_fmt(fmt), rows, cols, tokens)
+
+
+def canonical_bytes(fmt, rows: int, cols: int) -> int:
+    return _lib.tq_canonical_bytes(_fmt(fmt), rows, cols)
+
+
+def repacked_bytes(fmt, rows: int, cols: int) -> int:
+    return _lib.tq_repacked_bytes(_fmt(fmt), rows, cols)
+
+
+def repack(w_canonical: torch.Tensor, fmt, rows: int, cols: int, check_codes: bool = True, out=None) -> torch.Tensor:
+    """Canonical weights (uint8 CUDA tensor) -> repacked device layout (uint8).
+
+    With ``check_codes`` (pq2_0) the call waits for the repack and raises if any
+    2-bit code is 3, which pq2_0 does not use (load time only)."""
+    _need(w_canonical, torch.uint8, "w_canonical")
+    n = canonical_bytes(fmt, rows, cols)
+    if n == 0 or w_canonical.numel() != n:
+        raise ValueError(f"expected {n} canonical bytes for {fmt} {rows}x{cols}, got {w_canonical.numel()}")
+    dev = w_canonical.device
+    if out is None:
+        out = torch.empty(repacked_bytes(fmt, rows, cols), dtype=torch.uint8, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev) if check_codes else None
+    _check(_lib.tq_repack(_fmt(fmt), _ptr(w_canonical), _ptr(out), rows, cols, _ptr(flag), _stream()), "tq_repack")
+    if check_codes and _fmt(fmt) == FORMATS["pq2_0"] and int(flag.item()) != 0:
+        raise ValueError("pq2_0 matrix holds code 3, which is not a pq2_0 value")
+    return out
+
+
+def unrepack(w_repacked: torch.Tensor, fmt, rows: int, cols: int) -> torch.Tensor:
+    _need(w_repacked, torch.uint8, "w_repacked")
+    out = torch.empty(canonical_bytes(fmt, rows, cols), dtype=torch.uint8, device=w_repacked.device)
+    _check(_lib.tq_unrepack(_fmt(fmt), _ptr(w_repacked), _ptr(out), rows, cols, _stream()), "tq_unrepack")
+    return out
+
+
+def quantize_q8k(x: torch.Tensor, out=None):
+    """float32 [tokens, cols] -> (q int8 [T, cols], d float32 [T, cols/256], bsums int16 [T, cols/16])."""
+    _need(x, torch.float32, "x")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    T, K = x.shape
+    if out is None:
+        q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+        d = torch.empty((T, K // 256), dtype=torch.float32, device=x.device)
+        bs = torch.empty((T, K // 16), dtype=torch.int16, device=x.device)
+    else:
+        q, d, bs = out
+    _check(_lib.tq_quantize_q8k(_ptr(x), T, K, _ptr(q), _ptr(d), _ptr(bs), _stream()), "tq_quantize_q8k")
+    return q, d, bs
+
+
+def gemv(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None) -> torch.Tensor:
+    """y[rows] = W x for one q8_K token (q [cols] or [1, cols])."""
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _check(_lib.tq_gemv(_fmt(fmt), _ptr(w), rows, cols, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _stream()), "tq_gemv")
+    return out
+
+
+def gemm(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None) -> torch.Tensor:
+    """y[tokens, rows] for q8_K activations q [tokens, cols]."""
+    T = q.shape[0] if q.dim() == 2 else 1
+    if out is None:
+        out = torch.empty((T, rows), dtype=torch.float32, device=w.device)
+    _check(_lib.tq_gemm(_fmt(fmt), _ptr(w), rows, cols, T, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _stream()),
+           "tq_gemm")
+    return out
+
+
+def group_dots(fmt, w: torch.Tensor, rows: int, cols: int, q, bsums=None) -> torch.Tensor:
+    """Exact int32 group dots [tokens, rows, cols/128] from the product kernels."""
+    T = q.shape[0] if q.dim() == 2 else 1
+    out = torch.empty((T, rows, cols // 128), dtype=torch.int32, device=w.device)
+    _check(_lib.tq_group_dots(_fmt(fmt), _ptr(w), rows, cols, T, _ptr(q), _ptr(bsums), _ptr(out), _stream()),
+           "tq_group_dots")
+    return out
+
+
+class TernaryMatrix:
+    """A repacked weight matrix resident on the GPU, with its shape and format."""
+
+    def __init__(self, w_canonical: torch.Tensor, fmt: str, rows: int, cols: int):
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+        self.data = repack(w_canonical, fmt, rows, cols)
+
+    def matvec(self, q, d, bsums=None, out=None):
+        return gemv(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out)
+
+    def matmul(self, q, d, bsums=None, out=None):
+        return gemm(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out)
+
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        """fp32 activations [tokens, cols] -> fp32 [tokens, rows] (quantize, then product)."""
+        q, d, bs = quantize_q8k(x)
+        return self.matmul(q, d, bs)

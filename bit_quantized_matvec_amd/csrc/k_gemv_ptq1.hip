@@ -1,0 +1,190 @@
+// k_gemv_ptq1.hip -- decode matrix-vector product, repacked ptq1_0 x q8_K.
+//
+// Base-3 weights (page 1, "the detour that lost"; ciot README ptq1_0
+// paragraph): trit j of byte b is floor(3 * ((b * 3^j) mod 256) / 256), and
+// w = trit - 1.  The trits follow from one another: with v0 = b,
+// t_j = (3 v_j) >> 8 and v_{j+1} = (3 v_j) & 255.
+//
+// How (gfx950):
+//   * one lane = one row, a workgroup = a 64-row tile, waves split the
+//     8-group superblocks; 13 fully coalesced dwordx4 loads per row and
+//     superblock (1.75 bits per weight, bytes only reordered by the repack);
+//   * the four bytes of a code dword are split into two pairs of 16-bit lanes
+//     (bytes 0, 2 and bytes 1, 3), so one 32-bit multiply-by-3 advances two
+//     bytes at once without carries between them; each step yields a dword of
+//     four trits (one per byte) = one dot4 operand;
+//   * the trits are w + 1, so I = dot(t, q) - sum(q), the group sum coming
+//     from the q8_K partial sums (page 1, "the trick with 4 and 16": sum(y)
+//     over 128 values is one add over 8 partial sums);
+//   * the dot4 partner of trit j of four consecutive code bytes is the four
+//     activations 5 apart; each workgroup first writes this permuted copy of
+//     q into LDS, and the main loop reads it with wave-uniform (broadcast)
+//     LDS loads.  The two bytes per group that do not fill a dword are paired
+//     with the next group's, and their padding trits meet zero activations.
+#include "kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr int kMaxWaves = 8;
+constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h));
+}
+
+// Permuted activation table.  Entry (D < 48, j): bytes i = 0..3 hold
+// q[col(group gi, byte 4m + i, trit j)] with D = 6 gi + m.  Entry (48 + p, j, h):
+// the leftover dword p pairs bytes 24, 25 of groups 2p (h = 0) and 2p + 1
+// (h = 1); only the half of the dword that belongs to group 2p + h is non-zero.
+__device__ uint32_t table_entry(const int8_t* __restrict__ q, int G, int sb, int e) {
+  auto act = [&](int g, int byte, int j) -> uint32_t {
+    const int k = 5 * byte + j;  // position inside the group
+    if (g >= G || k >= 128) return 0u;
+    return (uint32_t)(uint8_t)q[(size_t)g * 128 + k];
+  };
+  if (e < 48 * 8) {
+    const int D = e >> 3, j = e & 7;
+    if (j >= 5) return 0u;
+    const int g = sb * 8 + D / 6, m = D % 6;
+    uint32_t r = 0;
+    for (int i = 0; i < 4; ++i) r |= act(g, 4 * m + i, j) << (8 * i);
+    return r;
+  }
+  const int f = e - 48 * 8;
+  const int p = f >> 4, jj = f & 15;
+  if (jj >= 10) return 0u;
+  const int j = jj >> 1, h = jj & 1;
+  const int g = sb * 8 + 2 * p + h;
+  const uint32_t lo = act(g, 24, j) | (act(g, 25, j) << 8);
+  return h ? lo << 16 : lo;
+}
+
+template <bool IDOTS>
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* __restrict__ codes,
+                                                                   const uint4* __restrict__ scales,
+                                                                   const int8_t* __restrict__ q, const float* __restrict__ dx,
+                                                                   const int16_t* __restrict__ bsums, float* __restrict__ y,
+                                                                   int32_t* __restrict__ idots, int rows, int G, int G8, int spw) {
+  extern __shared__ uint32_t table[];
+  __shared__ double red[kMaxWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int tile = blockIdx.x;
+  const int row = tile * 64 + lane;
+
+  for (int e = threadIdx.x; e < G8 * kTableDwords; e += blockDim.x)
+    table[e] = table_entry(q, G, e / kTableDwords, e % kTableDwords);
+  __syncthreads();
+
+  const int sb0 = wave * spw;
+  const int sb1 = min(G8, sb0 + spw);
+  double acc = 0.0;
+  for (int sb = sb0; sb < sb1; ++sb) {
+    // Loads 0..11 hold the 48 full dwords (3 loads per group pair), load 12
+    // the four leftover dwords.  One group pair is decoded per iteration,
+    // with the next pair's three loads already in flight.
+    const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
+    const uint4 left = cp[12 * 64];
+    const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
+    const uint32_t* tb = table + sb * kTableDwords;
+    uint4 cur[3] = {cp[0], cp[64], cp[128]};
+#pragma unroll 1
+    for (int gp = 0; gp < 4; ++gp) {
+      uint4 nxt[3] = {cur[0], cur[1], cur[2]};
+      if (gp < 3) {
+        nxt[0] = cp[(3 * gp + 3) * 64];
+        nxt[1] = cp[(3 * gp + 4) * 64];
+        nxt[2] = cp[(3 * gp + 5) * 64];
+      }
+      const uint32_t dws[13] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z,
+                                cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                                gp == 0 ? left.x : gp == 1 ? left.y : gp == 2 ? left.z : left.w};
+      int ia = 0, ib = 0;  // groups 2 gp and 2 gp + 1
+#pragma unroll
+      for (int m = 0; m < 13; ++m) {
+        const uint32_t d = dws[m];
+        uint32_t tv[10];
+        if (m < 12) {
+          const uint32_t* te = tb + (12 * gp + m) * 8;
+          const uint4 t0 = *reinterpret_cast<const uint4*>(te);
+          tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w; tv[4] = te[4];
+        } else {
+          const uint4* lt = reinterpret_cast<const uint4*>(tb + 48 * 8 + gp * 16);
+          const uint4 t0 = lt[0], t1 = lt[1];
+          const uint2 t2 = *reinterpret_cast<const uint2*>(lt + 2);
+          tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w;
+          tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w; tv[8] = t2.x; tv[9] = t2.y;
+        }
+        uint32_t e = d & 0x00FF00FFu;
+        uint32_t o = (d >> 8) & 0x00FF00FFu;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+          e *= 3u;
+          o *= 3u;
+          const int t = (int)(((e >> 8) & 0x00030003u) | (o & 0x03000300u));
+          if (m < 6) {
+            ia = __builtin_amdgcn_sdot4(t, (int)tv[j], ia, false);
+          } else if (m < 12) {
+            ib = __builtin_amdgcn_sdot4(t, (int)tv[j], ib, false);
+          } else {
+            ia = __builtin_amdgcn_sdot4(t, (int)tv[2 * j], ia, false);
+            ib = __builtin_amdgcn_sdot4(t, (int)tv[2 * j + 1], ib, false);
+          }
+          e &= 0x00FF00FFu;
+          o &= 0x00FF00FFu;
+        }
+      }
+      const uint32_t s2 = gp == 0 ? sc8.x : gp == 1 ? sc8.y : gp == 2 ? sc8.z : sc8.w;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = sb * 8 + 2 * gp + h;
+        if (g < G) {
+          const int16_t* bs = bsums + (size_t)g * 8;
+          const int qsum = bs[0] + bs[1] + bs[2] + bs[3] + bs[4] + bs[5] + bs[6] + bs[7];
+          const int I = (h ? ib : ia) - qsum;
+          if (IDOTS) {
+            if (row < rows) idots[(size_t)row * G + g] = I;
+          } else {
+            acc += ((double)half_bits_to_float(h ? (s2 >> 16) : (s2 & 0xffffu)) * (double)dx[g >> 1]) * (double)I;
+          }
+        }
+      }
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
+      cur[2] = nxt[2];
+    }
+  }
+  if (IDOTS) return;
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    double s = red[0][lane];
+    for (int w = 1; w < nw; ++w) s += red[w][lane];
+    if (row < rows) y[row] = (float)s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, const int16_t* bsums,
+                            float* y, int32_t* idots, hipStream_t s) {
+  const int G8 = (int)dm.G8;
+  int waves = G8 < kMaxWaves ? G8 : kMaxWaves;
+  const int spw = (G8 + waves - 1) / waves;
+  waves = (G8 + spw - 1) / spw;
+  const size_t lds = (size_t)G8 * kTableDwords * sizeof(uint32_t);
+  const uint4* codes = reinterpret_cast<const uint4*>(w);
+  const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
+  const dim3 grid((unsigned)dm.ntiles), block(64 * waves);
+  if (idots)
+    hipLaunchKernelGGL(gemv_ptq1_kernel<true>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
+                       (int)dm.G, G8, spw);
+  else
+    hipLaunchKernelGGL(gemv_ptq1_kernel<false>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
+                       (int)dm.G, G8, spw);
+  return hipGetLastError();
+}
+
+}  // namespace tq

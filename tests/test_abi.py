@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every declared symbol, and validates its
+arguments on the host.  No kernel is launched here: every call below fails
+validation before any HIP work (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import bit_quantized_matvec_amd as m
+
+    return m
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(tq):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(tq.lib(), n), n
+    assert set(names) == set(tq.EXPORTS)
+    assert tq.lib().tq_version() >= 100
+
+
+def test_sizes(tq):
+    # 34 and 28 bytes per 128 weights; repacked = canonical when rows % 64 == 0 and, for ptq1_0, groups % 8 == 0
+    assert tq.canonical_bytes("pq2_0", 32768, 8192) == 71303168
+    assert tq.repacked_bytes("pq2_0", 32768, 8192) == 71303168
+    assert tq.canonical_bytes("ptq1_0", 32768, 8192) == 58720256
+    assert tq.repacked_bytes("ptq1_0", 32768, 8192) == 58720256
+    assert tq.canonical_bytes("pq2_0", 17408, 5120) == 23674880
+    assert tq.repacked_bytes("pq2_0", 17408, 5120) == 23674880
+    # padding of the row tile (rows -> multiple of 64) and of ptq1_0 groups (-> multiple of 8)
+    assert tq.repacked_bytes("pq2_0", 1, 256) == 64 * 256 / 4 + 64 * 8 * 2  # codes + scales padded to 8 groups
+    assert tq.repacked_bytes("ptq1_0", 65, 256) == 2 * 8 * 64 * 28
+    assert tq.canonical_bytes("pq2_0", 0, 256) == 0
+    assert tq.repacked_bytes(7, 64, 256) == 0
+
+
+@pytest.mark.parametrize(
+    "fmt,rows,cols,tokens,expect",
+    [
+        (1, 64, 256, 1, 0),
+        (2, 5, 768, 3, 0),
+        (1, 0, 256, 1, -2),
+        (1, 64, 128, 1, -2),
+        (1, 64, 384, 1, -2),
+        (1, 64, 0, 1, -2),
+        (1, 64, 256, 0, -2),
+        (1, -3, 256, 1, -2),
+        (1, 1 << 27, 256, 1, -2),
+        (2, 64, 32768 + 256, 1, -2),
+        (2, 64, 32768, 1, 0),
+        (1, 64, 65536 + 256, 1, 0),
+        (0, 64, 256, 1, -4),
+        (3, 64, 256, 1, -4),
+    ],
+)
+def test_selector(tq, fmt, rows, cols, tokens, expect):
+    assert tq.check_shape(fmt, rows, cols, tokens) == expect
+
+
+def test_validation_errors_touch_nothing(tq):
+    L = tq.lib()
+    P = ctypes.c_void_p
+    good = P(0x100000)  # never dereferenced: each call below fails validation first
+    odd = P(0x100001)
+    # null pointers
+    assert L.tq_gemv(1, None, 64, 256, good, good, None, good, None) == tq.ERR_NULL
+    assert L.tq_gemv(1, good, 64, 256, good, None, None, good, None) == tq.ERR_NULL
+    assert L.tq_gemv(2, good, 64, 256, good, good, None, good, None) == tq.ERR_NULL  # ptq1_0 needs bsums
+    assert L.tq_gemm(1, good, 64, 256, 4, None, good, None, good, None) == tq.ERR_NULL
+    assert L.tq_quantize_q8k(None, 1, 256, good, good, good, None) == tq.ERR_NULL
+    assert L.tq_repack(1, None, good, 64, 256, None, None) == tq.ERR_NULL
+    assert L.tq_group_dots(1, good, 64, 256, 1, good, None, None, None) == tq.ERR_NULL
+    # alignment
+    assert L.tq_gemv(1, odd, 64, 256, good, good, None, good, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, odd, good, None, good, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, good, odd, None, good, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, good, good, None, P(0x100002), None) == tq.ERR_ALIGN
+    assert L.tq_gemv(2, good, 64, 256, good, good, odd, good, None) == tq.ERR_ALIGN
+    assert L.tq_quantize_q8k(P(0x100004), 1, 256, good, good, good, None) == tq.ERR_ALIGN
+    assert L.tq_repack(1, good, P(0x100008), 64, 256, None, None) == tq.ERR_ALIGN
+    # shapes and formats
+    assert L.tq_gemv(1, good, 64, 200, good, good, None, good, None) == tq.ERR_SHAPE
+    assert L.tq_gemm(1, good, 64, 256, 0, good, good, None, good, None) == tq.ERR_SHAPE
+    assert L.tq_quantize_q8k(good, 1, 100, good, good, good, None) == tq.ERR_SHAPE
+    assert L.tq_gemv(9, good, 64, 256, good, good, None, good, None) == tq.ERR_FORMAT
+    assert L.tq_unrepack(9, good, good, 64, 256, None) == tq.ERR_FORMAT
+    assert L.tq_last_hip_error() == 0
+
+
+def test_status_strings(tq):
+    L = tq.lib()
+    for s in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert len(L.tq_status_str(s)) > 0
+    with pytest.raises(tq.TQError) as e:
+        tq._check(tq.ERR_SHAPE, "x")
+    assert e.value.status == tq.ERR_SHAPE
+
+
+def test_no_cpu_fallback_in_binding():
+    """The binding never imports the oracle and has no CPU compute path."""
+    src = open(os.path.join(ROOT, "bit_quantized_matvec_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no CPU fallback", "")
+    for f in os.listdir(os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", f)).read().lower()

@@ -1,0 +1,332 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer results (q8_K fields, group dots, repacked bytes) must be bit-exact.
+Float outputs must satisfy, per output element (tolerance from the workload
+definition, 1e-5 relative per row):
+    |y_gpu - y_ref| <= 1e-5 * |y_ref|,   or, if y_ref == 0,
+    |y_gpu|         <= 1e-5 * sum_g |term_g|.
+Both sides evaluate the float epilogue in fp64 with exact terms, so in practice
+the outputs agree to the last bit; the tests also report how many do.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import tq_inputs as TI
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_matvec_amd as m
+
+    return m
+
+
+def dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    import torch
+
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_close_rows(y, ref, mag, rtol=1e-5, what=""):
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(y - ref)
+    bound = np.where(ref != 0, rtol * np.abs(ref), rtol * mag)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outputs outside tolerance; worst rel {np.max(err / np.maximum(np.abs(ref), 1e-300))}"
+    return int(np.sum(y == ref))
+
+
+def gpu_pipeline(tq, fmt, W, x):
+    """Repack, quantize and multiply on the GPU; returns numpy results."""
+    R, G, _ = W.shape
+    K = G * 128
+    T = x.shape[0]
+    Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
+    q, d, bs = tq.quantize_q8k(dev(x))
+    y = tq.gemm(fmt, Wd, R, K, q, d, bs) if T > 1 or fmt == "pq2_0" else tq.gemv(fmt, Wd, R, K, q, d, bs).view(1, R)
+    I = tq.group_dots(fmt, Wd, R, K, q, bs)
+    return Wd, host(q), host(d), host(bs), host(y).reshape(T, R), host(I)
+
+
+# --------------------------------------------------------------------------- q8_K
+
+
+def quant_cases():
+    g = TI.rng(77, 1)
+    yield "normal", TI.activations(g, 5, 8192)
+    yield "heavy_tails", (g.standard_t(2, size=(3, 2048)) * 10).astype(np.float32)
+    yield "subnormal", (g.standard_normal((2, 1024)) * 1e-40).astype(np.float32)
+    yield "tiny", (g.standard_normal((1, 512)) * 1e-44).astype(np.float32)
+    yield "huge", (g.uniform(-1, 1, size=(1, 512)) * 3e38).astype(np.float32)
+    x = np.zeros((2, 768), np.float32)
+    x[1, 300] = -2.5
+    x[1, 512:] = 7.0
+    yield "zeros_and_constants", x
+    rows = [l.split() for l in open(os.path.join(os.path.dirname(__file__), "golden", "q8k_ties.txt")) if l.strip() and not l.startswith("#")]
+    x = np.zeros((1, 256), np.float32)
+    x[0, 0] = 254
+    for i, (xv, _) in enumerate(rows[1:], start=1):
+        x[0, i] = float(xv)
+    yield "ties", x
+    yield "odd_tokens", TI.activations(g, 7, 256)
+
+
+@pytest.mark.parametrize("case", [c for c, _ in quant_cases()])
+def test_quantize_q8k_bit_exact(tq, orc, case):
+    x = dict(quant_cases())[case]
+    say("quantize", case, x.shape)
+    q, d, bs = tq.quantize_q8k(dev(x))
+    qo, do, bso = orc.quantize_q8k(x)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(d).view(np.uint32), do.view(np.uint32))
+    assert np.array_equal(host(bs), bso)
+
+
+# ------------------------------------------------------------------------- repack
+
+
+@pytest.mark.parametrize("fmt,R,K", [("pq2_0", 1, 256), ("pq2_0", 65, 768), ("pq2_0", 200, 2560),
+                                     ("ptq1_0", 1, 256), ("ptq1_0", 65, 768), ("ptq1_0", 130, 2304)])
+def test_repack_roundtrip(tq, fmt, R, K):
+    say("repack", fmt, R, K)
+    g = TI.rng(77, 2, R, K)
+    W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else g.integers(0, 256, size=(R, K // 128, 28), dtype=np.uint8)
+    Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
+    assert Wd.numel() == tq.repacked_bytes(fmt, R, K)
+    back = tq.unrepack(Wd, fmt, R, K)
+    assert np.array_equal(host(back), W.reshape(-1))
+
+
+def test_repack_flags_code_3(tq):
+    g = TI.rng(77, 3)
+    W = TI.pq2_matrix(g, 70, 512)
+    tq.repack(dev(W.reshape(-1)), "pq2_0", 70, 512)  # valid: no error
+    W[69, 3, 2 + 17] |= 0x30  # field 2 of one byte -> code 3
+    with pytest.raises(ValueError):
+        tq.repack(dev(W.reshape(-1)), "pq2_0", 70, 512)
+
+
+def test_one_hot_probes(tq, orc):
+    """A single non-zero weight times a one-hot activation locates every
+    (row, column) mapping of the repacked layout, for both formats."""
+    R, K = 67, 512
+    g = TI.rng(77, 4)
+    for fmt in ("pq2_0", "ptq1_0"):
+        cols = g.choice(K, size=24, replace=False)
+        rows = g.integers(0, R, size=24)
+        for r, c in zip(rows, cols):
+            if fmt == "pq2_0":
+                codes = np.full((R, K // 128, 32), 0x55, np.uint8)  # w = 0
+                k = c % 128
+                codes[r, c // 128, k >> 2] = (0x55 & ~(3 << (2 * (k & 3)))) | (2 << (2 * (k & 3)))  # w = +1
+                W = TI.assemble_pq2(codes, np.ones((R, K // 128), np.float16))
+            else:
+                zero = -(-256 * 121 // 243)  # encodes n = 121 = 11111 in base 3: every trit 1, every w 0
+                W = TI.assemble_ptq1(np.full((R, K // 128, 26), zero, np.uint8), np.ones((R, K // 128), np.float16))
+                k = c % 128
+                digits = [1] * 5
+                digits[k % 5] = 2  # w = +1 at trit k % 5
+                n = sum(dg * 3 ** (4 - j) for j, dg in enumerate(digits))
+                W[r, c // 128, 2 + k // 5] = -(-256 * n // 243)
+            x = np.zeros((1, K), np.float32)
+            x[0, c] = 1.0
+            _, _, _, y, I, = gpu_pipeline(tq, fmt, W, x)[1:]
+            yo = orc.matmul(fmt, W, *orc.quantize_q8k(x)[:2])
+            assert np.array_equal(y, yo), (fmt, r, c)
+            nz = np.argwhere(y[0] != 0).ravel().tolist()
+            assert nz == [r], (fmt, r, c, nz)
+            assert I[0, r, c // 128] == 127
+
+
+# ------------------------------------------------------------------ GEMV / GEMM grid
+
+
+GRID_R = [1, 4, 5, 12, 33, 64, 65, 200]
+GRID_K = [256, 512, 1024, 1280, 2304, 8192]
+
+
+@pytest.mark.parametrize("fmt", ["pq2_0", "ptq1_0"])
+def test_gemv_grid(tq, orc, fmt):
+    g = TI.rng(77, 5, 1 if fmt == "pq2_0" else 2)
+    exact = total = 0
+    for K in GRID_K:
+        for R in GRID_R:
+            say("gemv", fmt, R, K)
+            W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+            x = TI.activations(g, 1, K)
+            _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+            qo, do, bso = orc.quantize_q8k(x)
+            assert np.array_equal(q, qo) and np.array_equal(d, do) and np.array_equal(bs, bso)
+            assert np.array_equal(I, orc.group_dots(fmt, W, qo)), (fmt, R, K)
+            yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+            exact += assert_close_rows(y, yo, mag, what=f"{fmt} {R}x{K}")
+            total += y.size
+    say(f"gemv {fmt}: {exact}/{total} outputs bit-identical to the oracle")
+
+
+GEMM_T = [2, 3, 4, 5, 7, 8, 16, 17, 33, 64, 65, 100]
+
+
+@pytest.mark.parametrize("R,K", [(1, 256), (33, 1280), (64, 2048), (130, 512)])
+def test_gemm_grid(tq, orc, R, K):
+    g = TI.rng(77, 6, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    exact = total = 0
+    for T in GEMM_T:
+        say("gemm", R, K, T)
+        x = TI.activations(g, T, K)
+        Wd, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
+        qo, do, _ = orc.quantize_q8k(x)
+        assert np.array_equal(q, qo) and np.array_equal(d, do)
+        assert np.array_equal(I, orc.group_dots("pq2_0", W, qo)), (R, K, T)
+        yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
+        exact += assert_close_rows(y, yo, mag, what=f"gemm {R}x{K} T={T}")
+        total += y.size
+        # one matrix-vector product per token gives the same outputs
+        qd, dd, bd = tq.quantize_q8k(dev(x))
+        for t in (0, T - 1):
+            yv = host(tq.gemv("pq2_0", Wd, R, K, qd[t], dd[t]))
+            assert_close_rows(yv, yo[t], mag[t], what=f"gemv token {t}")
+    say(f"gemm {R}x{K}: {exact}/{total} outputs bit-identical to the oracle")
+
+
+def test_degenerate_inputs(tq, orc):
+    g = TI.rng(77, 7)
+    R, K = 70, 1024
+    W = TI.pq2_matrix(g, R, K)
+    # zero activations: d = 0, q = 0, y = 0 exactly
+    for T in (1, 3):
+        _, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, np.zeros((T, K), np.float32))
+        assert not q.any() and not d.any() and not bs.any() and not I.any() and np.all(y == 0)
+    # zero weights (w = 0 everywhere) give exactly 0
+    W0 = TI.assemble_pq2(np.full((R, K // 128, 32), 0x55, np.uint8), TI.scales_f16(g, R, K))
+    _, _, _, _, y, I = gpu_pipeline(tq, "pq2_0", W0, TI.activations(g, 5, K))
+    assert not I.any() and np.all(y == 0)
+    # all +1 and all -1 (u = 2 in every slot position, the slot-3 sign hazard of the pages)
+    Wp = TI.assemble_pq2(np.full((R, K // 128, 32), 0xAA, np.uint8), TI.scales_f16(g, R, K))
+    Wm = TI.assemble_pq2(np.full((R, K // 128, 32), 0x00, np.uint8), TI.scales_f16(g, R, K))
+    xe = np.full((2, K), 127.0, np.float32)
+    xe[1] *= -1
+    _, _, _, _, yp, Ip = gpu_pipeline(tq, "pq2_0", Wp, xe)
+    _, _, _, _, ym, Im = gpu_pipeline(tq, "pq2_0", Wm, xe)
+    assert np.all(Ip[0] == 128 * 127) and np.all(Ip[1] == -128 * 127) and np.array_equal(Im, -Ip)
+    qo, do, _ = orc.quantize_q8k(xe)
+    assert np.array_equal(yp, orc.matmul("pq2_0", Wp, qo, do))
+
+
+def test_deterministic_and_stream(tq):
+    import torch
+
+    g = TI.rng(77, 8)
+    R, K = 300, 4096
+    W = TI.pq2_matrix(g, R, K)
+    x = TI.activations(g, 9, K)
+    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    q, d, bs = tq.quantize_q8k(dev(x))
+    a = host(tq.gemm("pq2_0", Wd, R, K, q, d))
+    b = host(tq.gemm("pq2_0", Wd, R, K, q, d))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = tq.gemm("pq2_0", Wd, R, K, q, d)
+    s.synchronize()
+    assert np.array_equal(a, b) and np.array_equal(a, c.cpu().numpy())
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+
+def test_tiny_workload_full(tq, orc):
+    fmt, W, x = TI.make("tiny_256x1024")
+    say("tiny 256x1024")
+    _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    qo, do, bso = orc.quantize_q8k(x)
+    assert np.array_equal(q, qo) and np.array_equal(d, do) and np.array_equal(bs, bso)
+    assert np.array_equal(I, orc.group_dots(fmt, W, qo))
+    yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+    assert_close_rows(y, yo, mag, what="tiny")
+
+
+@pytest.mark.parametrize("name", ["decode_32768x8192", "ptq1_32768x8192"])
+def test_decode_workload_full(tq, orc, name):
+    """Every output of the full-size matrix-vector product against the oracle."""
+    fmt, W, x = TI.make(name)
+    say(name)
+    R, G, _ = W.shape
+    _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    qo, do, bso = orc.quantize_q8k(x)
+    assert np.array_equal(q, qo) and np.array_equal(d, do) and np.array_equal(bs, bso)
+    assert np.array_equal(I, orc.group_dots(fmt, W, qo, threads=THREADS))
+    yo, mag = orc.matmul(fmt, W, qo, do, threads=THREADS, with_mag=True)
+    exact = assert_close_rows(y, yo, mag, what=name)
+    say(f"{name}: {exact}/{y.size} outputs bit-identical")
+
+
+@pytest.mark.parametrize("T", [4, 64])
+def test_prefill_workload_sampled(tq, orc, T):
+    """17408 x 5120 at 4 and 64 tokens: q8_K in full, outputs on sampled rows
+    (first and last tile included) against the oracle."""
+    fmt, W, x = TI.make("prefill_17408x5120_t64" if T == 64 else "prefill_17408x5120_t4")
+    say("prefill", T)
+    R = W.shape[0]
+    _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    qo, do, bso = orc.quantize_q8k(x)
+    assert np.array_equal(q, qo) and np.array_equal(d, do) and np.array_equal(bs, bso)
+    g = TI.rng(77, 9, T)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(R - 64, R), g.integers(0, R, size=192)]))
+    yo, mag = orc.matmul_rows(fmt, W, qo, do, rows, with_mag=True)
+    assert_close_rows(y[:, rows], yo, mag, what=f"prefill T={T}")
+    assert np.array_equal(I[:, rows[:40], :], orc.group_dots_rows(fmt, W, qo, rows[:40]))
+
+
+def test_step64_shapes_sampled(tq, orc):
+    """The five matrix shapes of the synthetic 64-layer decode step (one layer),
+    each with its own fresh activation vector, sampled rows vs the oracle."""
+    for mi, (name, R, K) in enumerate(TI.STEP64_SHAPES):
+        say("step64 shape", name, R, K)
+        g = TI.rng(TI.STEP64, 0, mi)
+        W = TI.pq2_matrix(g, R, K)
+        x = TI.activations(g, 1, K)
+        _, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
+        qo, do, _ = orc.quantize_q8k(x)
+        assert np.array_equal(q, qo) and np.array_equal(d, do)
+        rows = np.unique(np.concatenate([np.arange(32), np.arange(R - 32, R), TI.rng(77, 10, mi).integers(0, R, 96)]))
+        yo, mag = orc.matmul_rows("pq2_0", W, qo, do, rows, with_mag=True)
+        assert_close_rows(y[0, rows], yo[0], mag[0], what=name)
+        assert np.array_equal(I[:, rows, :], orc.group_dots_rows("pq2_0", W, qo, rows))
+
+
+def test_max_columns(tq, orc):
+    g = TI.rng(77, 11)
+    for fmt, K in (("pq2_0", 65536), ("ptq1_0", 32768)):
+        say("max cols", fmt, K)
+        W = TI.pq2_matrix(g, 3, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, 3, K)
+        x = TI.activations(g, 1, K)
+        _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+        qo, do, _ = orc.quantize_q8k(x)
+        assert np.array_equal(I, orc.group_dots(fmt, W, qo))
+        yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+        assert_close_rows(y, yo, mag, what=f"max cols {fmt}")
