@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_matvec_amd.build` first")
+    raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_matvec_amd/build.py` first")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -34,8 +34,9 @@ _SIGS = {
     "tq_repack": ([_i32, _p, _p, _i64, _i64, _p, _p], _i32),
     "tq_unrepack": ([_i32, _p, _p, _i64, _i64, _p], _i32),
     "tq_quantize_q8k": ([_p, _i64, _i64, _p, _p, _p, _p], _i32),
-    "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p], _i32),
-    "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p], _i32),
+    "tq_workspace_bytes": ([_i32, _i64, _i64, _i64], _i64),
+    "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
+    "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_group_dots": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_status_str": ([_i32], ctypes.c_char_p),
     "tq_last_hip_error": ([], _i32),
@@ -143,21 +144,31 @@ def quantize_q8k(x: torch.Tensor, out=None):
     return q, d, bs
 
 
-def gemv(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None) -> torch.Tensor:
-    """y[rows] = W x for one q8_K token (q [cols] or [1, cols])."""
+def workspace_bytes(fmt, rows: int, cols: int, tokens: int = 1) -> int:
+    return _lib.tq_workspace_bytes(_fmt(fmt), rows, cols, tokens)
+
+
+def workspace(fmt, rows: int, cols: int, tokens: int = 1, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for tq_gemv / tq_gemm of this shape (reusable)."""
+    return torch.zeros(max(16, workspace_bytes(fmt, rows, cols, tokens)), dtype=torch.uint8, device=device)
+
+
+def gemv(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None, ws=None) -> torch.Tensor:
+    """y[rows] = W x for one q8_K token (q [cols] or [1, cols]); ws: optional workspace."""
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=w.device)
-    _check(_lib.tq_gemv(_fmt(fmt), _ptr(w), rows, cols, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _stream()), "tq_gemv")
+    _check(_lib.tq_gemv(_fmt(fmt), _ptr(w), rows, cols, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _ptr(ws),
+                        _stream()), "tq_gemv")
     return out
 
 
-def gemm(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None) -> torch.Tensor:
-    """y[tokens, rows] for q8_K activations q [tokens, cols]."""
+def gemm(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None, ws=None) -> torch.Tensor:
+    """y[tokens, rows] for q8_K activations q [tokens, cols]; ws: optional workspace."""
     T = q.shape[0] if q.dim() == 2 else 1
     if out is None:
         out = torch.empty((T, rows), dtype=torch.float32, device=w.device)
-    _check(_lib.tq_gemm(_fmt(fmt), _ptr(w), rows, cols, T, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _stream()),
-           "tq_gemm")
+    _check(_lib.tq_gemm(_fmt(fmt), _ptr(w), rows, cols, T, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _ptr(ws),
+                        _stream()), "tq_gemm")
     return out
 
 
@@ -176,12 +187,13 @@ class TernaryMatrix:
     def __init__(self, w_canonical: torch.Tensor, fmt: str, rows: int, cols: int):
         self.fmt, self.rows, self.cols = fmt, rows, cols
         self.data = repack(w_canonical, fmt, rows, cols)
+        self.ws = workspace(fmt, rows, cols, device=w_canonical.device)
 
     def matvec(self, q, d, bsums=None, out=None):
-        return gemv(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out)
+        return gemv(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out, self.ws)
 
     def matmul(self, q, d, bsums=None, out=None):
-        return gemm(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out)
+        return gemm(self.fmt, self.data, self.rows, self.cols, q, d, bsums, out, self.ws)
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         """fp32 activations [tokens, cols] -> fp32 [tokens, rows] (quantize, then product)."""

@@ -1,6 +1,7 @@
 """Compile the HIP sources of libtq for gfx950 into an in-tree shared library.
 
-Run as ``python -m bit_quantized_matvec_amd.build``.  Always recompiles.
+Run as ``python bit_quantized_matvec_amd/build.py`` (it does not import the
+package, whose import loads the library).  Always recompiles.
 Every HIP translation unit is built with packed FP32 instructions disabled and
 without fast-math (the q8_K quantizer relies on IEEE division and rounding).
 """

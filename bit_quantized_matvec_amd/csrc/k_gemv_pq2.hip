@@ -7,25 +7,44 @@
 // How (gfx950): the product streams every weight byte from HBM exactly once,
 // so the kernel is bandwidth bound and is shaped for coalesced loads and
 // memory-level parallelism rather than for ALU reuse.
-//   * one lane = one row; a workgroup = one 64-row tile; its waves split the
-//     columns into contiguous runs of 256-column superchunks;
-//   * per superchunk a lane issues four dwordx4 loads (qd = 0..3), each a
-//     fully coalesced 1 KiB wave request; UNROLL superchunks are in flight;
+//   * one lane = one row; a workgroup = one 64-row tile and one slice of the
+//     columns; its waves split the slice into runs of 256-column superchunks;
+//   * per superchunk a lane issues four non-temporal dwordx4 loads (qd = 0..3),
+//     each a fully coalesced 1 KiB wave request (the codes are never reused);
 //   * the activation bytes a lane needs are the same for every lane of the
-//     wave, so they are read with scalar loads into SGPRs and fed to
-//     v_dot4_i32_i8 directly -- no LDS traffic, no VGPRs;
+//     wave, so they come in with scalar loads and feed v_dot4_i32_i8 from
+//     SGPRs -- no LDS traffic, no VGPRs;
 //   * each code dword yields four dot4 operands with one shift and one mask
-//     each ((d << (6-2s)) & 0xC0C0C0C0 = 64*w for four columns, the slot
-//     masking idea of the pages with two's-complement codes, so no +1
-//     correction is needed); the factor 64 is removed exactly by a shift;
+//     each ((d << (6-2s)) & 0xC0C0C0C0 = 64*w for four columns: the pages'
+//     slot masking, with two's-complement codes so that no +1 correction is
+//     needed); the factor 64 is removed exactly by a shift;
 //   * per group: term = (d_w * d_x) * I in fp64 (exact), accumulated in fp64;
-//     the wave partials are combined in LDS in wave order and rounded once.
+//   * the wave partials of a workgroup are summed in LDS in wave order.  With
+//     several column slices per tile (more, smaller workgroups, so the
+//     hardware can balance them over the CUs), each workgroup stores its fp64
+//     partial in a workspace and bumps the tile's counter; the last one to
+//     arrive sums the slices in slice order, writes y and resets the counter.
+//     The result is therefore deterministic, and no memset is needed between
+//     calls (safe inside a captured graph).
 #include "kernels.h"
 
 namespace tq {
 namespace {
 
 constexpr int kMaxWaves = 16;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Weight codes are read once and never reused: non-temporal loads keep them
+// from displacing reusable lines and stream measurably faster on gfx950.
+template <bool NT>
+__device__ __forceinline__ uint4 load_codes(const uint4* p) {
+  if (NT) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return uint4{t.x, t.y, t.z, t.w};
+  }
+  return *p;
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h));
@@ -57,24 +76,33 @@ __device__ __forceinline__ void superchunk_dots(const uint4 (&v)[4], const int* 
   }
 }
 
-template <int UNROLL, bool IDOTS>
+}  // namespace
+
+// grid = (ntiles, slices).  Workgroup (tile, slice) covers superchunks
+// [slice * scw, min(nsc, (slice + 1) * scw)); its waves take runs of spw.
+template <int UNROLL, bool IDOTS, bool NT>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* __restrict__ codes,
                                                                   const uint32_t* __restrict__ scales,
                                                                   const int* __restrict__ q, const float* __restrict__ dx,
                                                                   float* __restrict__ y, int32_t* __restrict__ idots,
-                                                                  int rows, int nsc, int G8, int spw) {
+                                                                  int rows, int nsc, int G8, int scw, int spw,
+                                                                  double* __restrict__ partials, unsigned* __restrict__ counters) {
   __shared__ double red[kMaxWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int tile = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int nslices = gridDim.y;
   const int row = tile * 64 + lane;
   const int G = 2 * nsc;
-  const int sc0 = wave * spw;
-  const int sc1 = min(nsc, sc0 + spw);
+  const int wg0 = slice * scw;
+  const int wg1 = min(nsc, wg0 + scw);
+  const int sc0 = min(wg1, wg0 + wave * spw);
+  const int sc1 = min(wg1, sc0 + spw);
 
   const uint4* cp = codes + (size_t)tile * nsc * 256 + lane;
-  const uint32_t* sp = scales + (size_t)tile * G8 * 256 + lane * 4;
+  const uint32_t* sp = scales + (size_t)tile * nsc * 64 + lane;
   double acc = 0.0;
 
   auto epilogue = [&](int sc, int i0, int i1) {
@@ -85,7 +113,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
         idots[(size_t)row * G + 2 * sc + 1] = I1;
       }
     } else {
-      const uint32_t s2 = sp[(sc >> 2) * 256 + (sc & 3)];  // fp16 scales of groups 2sc, 2sc+1
+      const uint32_t s2 = sp[sc * 64];  // fp16 scales of groups 2sc, 2sc+1
       const double dxs = (double)dx[sc];
       acc += ((double)half_bits_to_float(s2 & 0xffffu) * dxs) * (double)I0;
       acc += ((double)half_bits_to_float(s2 >> 16) * dxs) * (double)I1;
@@ -98,7 +126,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) v[u][qd] = cp[(size_t)((sc + u) * 4 + qd) * 64];
+      for (int qd = 0; qd < 4; ++qd) v[u][qd] = load_codes<NT>(cp + (size_t)((sc + u) * 4 + qd) * 64);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       int i0 = 0, i1 = 0;
@@ -109,7 +137,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
   for (; sc < sc1; ++sc) {
     uint4 v[4];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) v[qd] = cp[(size_t)(sc * 4 + qd) * 64];
+    for (int qd = 0; qd < 4; ++qd) v[qd] = load_codes<NT>(cp + (size_t)(sc * 4 + qd) * 64);
     int i0 = 0, i1 = 0;
     superchunk_dots(v, q + (size_t)sc * 64, i0, i1);
     epilogue(sc, i0, i1);
@@ -118,33 +146,80 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
   if (IDOTS) return;
   red[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    double s = red[0][lane];
-    for (int w = 1; w < nw; ++w) s += red[w][lane];
+  if (wave != 0) return;
+  double s = red[0][lane];
+  for (int w = 1; w < nw; ++w) s += red[w][lane];
+  if (nslices == 1) {
     if (row < rows) y[row] = (float)s;
+    return;
   }
+  // The partial goes out with an agent-scope atomic store (written through
+  // to the level shared by all XCDs, so no whole-L2 write-back is needed);
+  // the counter is bumped only after the store has completed (vmcnt = 0).
+  __hip_atomic_store(&partials[((size_t)tile * nslices + slice) * 64 + lane], s, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  if (prev != (unsigned)(nslices - 1)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  double t = 0.0;
+  for (int k = 0; k < nslices; ++k)
+    t += __hip_atomic_load(&partials[((size_t)tile * nslices + k) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (row < rows) y[row] = (float)t;
+  if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-}  // namespace
-
-hipError_t launch_gemv_pq2(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
-                           int32_t* idots, hipStream_t s) {
-  constexpr int kUnroll = 4;
+GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace) {
+  // Measured on MI355X: with 384 or more row tiles one workgroup per tile is
+  // fastest (the extra workgroups of a split only add reduction work); with
+  // fewer tiles, splitting the columns until there are ~384 workgroups (each
+  // keeping at least 4 superchunks) fills the chip.  Up to 4 waves per
+  // workgroup, each with a run of superchunks.
+  GemvPlan p;
   const int nsc = (int)dm.nsc;
-  // Split the columns over up to 8 waves, each taking a contiguous run.
-  int waves = nsc < 8 ? nsc : 8;
-  const int spw = (nsc + waves - 1) / waves;
-  waves = (nsc + spw - 1) / spw;
+  int slices = 1;
+  if (have_workspace && dm.ntiles < 384) {
+    slices = (int)((384 + dm.ntiles - 1) / dm.ntiles);
+    slices = slices < kMaxSlices ? slices : kMaxSlices;
+    const int most = nsc / 4 > 1 ? nsc / 4 : 1;
+    slices = slices < most ? slices : most;
+  }
+  p.scw = (nsc + slices - 1) / slices;
+  p.slices = (nsc + p.scw - 1) / p.scw;
+  const int waves = p.scw < 4 ? p.scw : 4;
+  p.spw = (p.scw + waves - 1) / waves;
+  p.waves = (p.scw + p.spw - 1) / p.spw;
+  return p;
+}
+
+hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
+                                int32_t* idots, void* workspace, const GemvPlan& p, hipStream_t s) {
+  constexpr int kUnroll = 2;
+  const int nsc = (int)dm.nsc;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
-  const dim3 grid((unsigned)dm.ntiles), block(64 * waves);
+  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
+  double* partials =
+      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   if (idots)
-    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, true>), grid, block, 0, s, codes, scales,
-                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, spw);
+    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, true, true>), grid, block, 0, s, codes, scales,
+                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, p.scw, p.spw,
+                       partials, counters);
   else
-    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, false>), grid, block, 0, s, codes, scales,
-                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, spw);
+    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, false, true>), grid, block, 0, s, codes, scales,
+                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, p.scw, p.spw,
+                       partials, counters);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_pq2(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
+                           int32_t* idots, void* workspace, hipStream_t s) {
+  const GemvPlan p = plan_gemv_pq2(dm, workspace != nullptr && idots == nullptr);
+  return launch_gemv_pq2_plan(w, dm, q, dx, y, idots, workspace, p, s);
 }
 
 }  // namespace tq

@@ -60,26 +60,37 @@ __device__ uint32_t table_entry(const int8_t* __restrict__ q, int G, int sb, int
   return h ? lo << 16 : lo;
 }
 
+}  // namespace
+
+// grid = (ntiles, slices).  Workgroup (tile, slice) covers superblocks
+// [slice * scw, min(G8, (slice + 1) * scw)); its waves take runs of spw.
 template <bool IDOTS>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* __restrict__ codes,
                                                                    const uint4* __restrict__ scales,
                                                                    const int8_t* __restrict__ q, const float* __restrict__ dx,
                                                                    const int16_t* __restrict__ bsums, float* __restrict__ y,
-                                                                   int32_t* __restrict__ idots, int rows, int G, int G8, int spw) {
+                                                                   int32_t* __restrict__ idots, int rows, int G, int G8,
+                                                                   int scw, int spw, double* __restrict__ partials,
+                                                                   unsigned* __restrict__ counters) {
   extern __shared__ uint32_t table[];
   __shared__ double red[kMaxWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int tile = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int nslices = gridDim.y;
   const int row = tile * 64 + lane;
+  const int wg0 = slice * scw;
+  const int wg1 = min(G8, wg0 + scw);
 
-  for (int e = threadIdx.x; e < G8 * kTableDwords; e += blockDim.x)
-    table[e] = table_entry(q, G, e / kTableDwords, e % kTableDwords);
+  // permuted activations of this workgroup's superblocks
+  for (int e = threadIdx.x; e < (wg1 - wg0) * kTableDwords; e += blockDim.x)
+    table[e] = table_entry(q, G, wg0 + e / kTableDwords, e % kTableDwords);
   __syncthreads();
 
-  const int sb0 = wave * spw;
-  const int sb1 = min(G8, sb0 + spw);
+  const int sb0 = min(wg1, wg0 + wave * spw);
+  const int sb1 = min(wg1, sb0 + spw);
   double acc = 0.0;
   for (int sb = sb0; sb < sb1; ++sb) {
     // Loads 0..11 hold the 48 full dwords (3 loads per group pair), load 12
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
     const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
     const uint4 left = cp[12 * 64];
     const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
-    const uint32_t* tb = table + sb * kTableDwords;
+    const uint32_t* tb = table + (sb - wg0) * kTableDwords;
     uint4 cur[3] = {cp[0], cp[64], cp[128]};
 #pragma unroll 1
     for (int gp = 0; gp < 4; ++gp) {
@@ -159,32 +170,75 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
   if (IDOTS) return;
   red[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    double s = red[0][lane];
-    for (int w = 1; w < nw; ++w) s += red[w][lane];
+  if (wave != 0) return;
+  double s = red[0][lane];
+  for (int w = 1; w < nw; ++w) s += red[w][lane];
+  if (nslices == 1) {
     if (row < rows) y[row] = (float)s;
+    return;
   }
+  // several slices per tile: the last workgroup to arrive sums them in order
+  // The partial goes out with an agent-scope atomic store (written through
+  // to the level shared by all XCDs, so no whole-L2 write-back is needed);
+  // the counter is bumped only after the store has completed (vmcnt = 0).
+  __hip_atomic_store(&partials[((size_t)tile * nslices + slice) * 64 + lane], s, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  if (prev != (unsigned)(nslices - 1)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  double t = 0.0;
+  for (int k = 0; k < nslices; ++k)
+    t += __hip_atomic_load(&partials[((size_t)tile * nslices + k) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (row < rows) y[row] = (float)t;
+  if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-}  // namespace
-
-hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, const int16_t* bsums,
-                            float* y, int32_t* idots, hipStream_t s) {
+GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
+  // As for pq2_0: one workgroup per tile when there are many tiles, else split
+  // the 8-group superblocks until there are ~384 workgroups.
+  GemvPlan p;
   const int G8 = (int)dm.G8;
-  int waves = G8 < kMaxWaves ? G8 : kMaxWaves;
-  const int spw = (G8 + waves - 1) / waves;
-  waves = (G8 + spw - 1) / spw;
-  const size_t lds = (size_t)G8 * kTableDwords * sizeof(uint32_t);
+  int slices = 1;
+  if (have_workspace && dm.ntiles < 384) {
+    slices = (int)((384 + dm.ntiles - 1) / dm.ntiles);
+    slices = slices < kMaxSlices ? slices : kMaxSlices;
+    slices = slices < G8 ? slices : G8;
+  }
+  p.scw = (G8 + slices - 1) / slices;
+  p.slices = (G8 + p.scw - 1) / p.scw;
+  const int waves = p.scw < kMaxWaves ? p.scw : kMaxWaves;
+  p.spw = (p.scw + waves - 1) / waves;
+  p.waves = (p.scw + p.spw - 1) / p.spw;
+  return p;
+}
+
+hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
+                                 const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,
+                                 hipStream_t s) {
+  const size_t lds = (size_t)p.scw * kTableDwords * sizeof(uint32_t);
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
-  const dim3 grid((unsigned)dm.ntiles), block(64 * waves);
+  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
+  double* partials =
+      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   if (idots)
     hipLaunchKernelGGL(gemv_ptq1_kernel<true>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
-                       (int)dm.G, G8, spw);
+                       (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters);
   else
     hipLaunchKernelGGL(gemv_ptq1_kernel<false>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
-                       (int)dm.G, G8, spw);
+                       (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, const int16_t* bsums,
+                            float* y, int32_t* idots, void* workspace, hipStream_t s) {
+  const GemvPlan p = plan_gemv_ptq1(dm, workspace != nullptr && idots == nullptr);
+  return launch_gemv_ptq1_plan(w, dm, q, dx, bsums, y, idots, workspace, p, s);
 }
 
 }  // namespace tq

@@ -57,8 +57,8 @@ __global__ void repack_pq2_codes(const uint8_t* __restrict__ src, uint32_t* __re
 }
 
 // Inverse: one thread per canonical 34-byte block.
-__global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                   uint8_t* __restrict__ dst, int64_t rows, int64_t nsc, int64_t G8) {
+__global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ scales,
+                                   uint8_t* __restrict__ dst, int64_t rows, int64_t nsc) {
   const int64_t G = nsc * 2;
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (b >= rows * G) return;
@@ -67,7 +67,8 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
   const int r = (int)(row % kRowTile);
   const int64_t sc = g >> 1;
   uint8_t* out = dst + b * 34;
-  const uint16_t h = scales[((tile * G8 + g / 8) * 64 + r) * 8 + g % 8];
+  const uint32_t pair = scales[(tile * nsc + sc) * 64 + r];
+  const uint32_t h = (g & 1) ? pair >> 16 : pair & 0xffffu;
   out[0] = (uint8_t)(h & 0xff);
   out[1] = (uint8_t)(h >> 8);
   for (int qd = 0; qd < 4; ++qd) {
@@ -87,7 +88,28 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
   }
 }
 
-// ------------------------------------------------------------- scales (both)
+// ------------------------------------------------------------- pq2_0 scales
+// fp16 scales of groups 2 sc, 2 sc + 1 of a row into one dword of
+// [tile][sc][row]; zero for padding rows.
+__global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows, int64_t nsc,
+                                  int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const int r = (int)(i & 63);
+  const int64_t rest = i >> 6;
+  const int64_t sc = rest % nsc;
+  const int64_t tile = rest / nsc;
+  const int64_t row = tile * kRowTile + r;
+  uint32_t v = 0;
+  if (row < rows) {
+    const uint8_t* b0 = src + (row * 2 * nsc + 2 * sc) * 34;
+    const uint8_t* b1 = b0 + 34;
+    v = (uint32_t)(b0[0] | (b0[1] << 8)) | ((uint32_t)(b1[0] | (b1[1] << 8)) << 16);
+  }
+  dst[i] = v;
+}
+
+// ------------------------------------------------------------- ptq1_0 scales
 // fp16 scale of (row, group) into [tile][g8][row][8]; zero for padding.
 __global__ void repack_scales(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows, int64_t G,
                               int64_t G8, int block_bytes, int64_t n) {
@@ -183,16 +205,16 @@ hipError_t launch_repack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, i
                      dm.rows, dm.nsc, ndw, bad_flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ns = scale_bytes(dm) / 2;
-  hipLaunchKernelGGL(repack_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src,
-                     reinterpret_cast<uint16_t*>(dst + pq2_code_bytes(dm)), dm.rows, dm.G, dm.G8, 34, ns);
+  const int64_t ns = pq2_scale_bytes(dm) / 4;
+  hipLaunchKernelGGL(repack_pq2_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src,
+                     reinterpret_cast<uint32_t*>(dst + pq2_code_bytes(dm)), dm.rows, dm.nsc, ns);
   return hipGetLastError();
 }
 
 hipError_t launch_unrepack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, hipStream_t s) {
   const int64_t nb = dm.rows * dm.G;
   hipLaunchKernelGGL(unrepack_pq2_codes, dim3(grid_for(nb)), dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(src),
-                     reinterpret_cast<const uint16_t*>(src + pq2_code_bytes(dm)), dst, dm.rows, dm.nsc, dm.G8);
+                     reinterpret_cast<const uint32_t*>(src + pq2_code_bytes(dm)), dst, dm.rows, dm.nsc);
   return hipGetLastError();
 }
 
@@ -202,7 +224,7 @@ hipError_t launch_repack_ptq1(const uint8_t* src, uint8_t* dst, const Dims& dm, 
                      dm.rows, dm.G, dm.G8, ndw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ns = scale_bytes(dm) / 2;
+  const int64_t ns = ptq1_scale_bytes(dm) / 2;
   hipLaunchKernelGGL(repack_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src,
                      reinterpret_cast<uint16_t*>(dst + ptq1_code_bytes(dm)), dm.rows, dm.G, dm.G8, 28, ns);
   return hipGetLastError();

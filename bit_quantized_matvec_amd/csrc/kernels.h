@@ -8,6 +8,22 @@
 
 namespace tq {
 
+// Split of a matrix-vector product over workgroups: `slices` column slices per
+// 64-row tile of `scw` superchunks (or 8-group superblocks for ptq1_0) each,
+// `waves` waves per workgroup taking runs of `spw`.
+struct GemvPlan {
+  int slices, scw, waves, spw;
+};
+constexpr int kMaxSlices = 16;
+// s_waitcnt immediate for "vmcnt(0)" on gfx9-family targets (vmcnt in bits
+// 3:0 and 15:14 = 0; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Workspace of the split products: per-tile arrival counters (zero between
+// calls), then fp64 partial sums [tile][slice][64].
+inline int64_t workspace_counter_bytes(const Dims& d) { return (d.ntiles * 4 + 255) / 256 * 256; }
+inline int64_t workspace_bytes(const Dims& d) { return workspace_counter_bytes(d) + d.ntiles * kMaxSlices * 64 * 8; }
+
 hipError_t launch_quantize_q8k(const float* x, int64_t nblocks, int8_t* q, float* d, int16_t* bsums, hipStream_t s);
 
 hipError_t launch_repack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, int32_t* bad_flag, hipStream_t s);
@@ -16,10 +32,19 @@ hipError_t launch_repack_ptq1(const uint8_t* src, uint8_t* dst, const Dims& dm, 
 hipError_t launch_unrepack_ptq1(const uint8_t* src, uint8_t* dst, const Dims& dm, hipStream_t s);
 
 // y[rows] (fp32) or, if idots != nullptr, the int32 group dots [rows][G].
+// With a workspace (workspace_bytes, zeroed before first use) the columns are
+// split over several workgroups per tile; without one, one workgroup per tile.
+GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace);
+hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
+                                int32_t* idots, void* workspace, const GemvPlan& p, hipStream_t s);
 hipError_t launch_gemv_pq2(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
-                           int32_t* idots, hipStream_t s);
+                           int32_t* idots, void* workspace, hipStream_t s);
+GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace);
+hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
+                                 const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,
+                                 hipStream_t s);
 hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
-                            const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
+                            const int16_t* bsums, float* y, int32_t* idots, void* workspace, hipStream_t s);
 // y[tokens][rows] or idots [tokens][rows][G].
 hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                            float* y, int32_t* idots, hipStream_t s);

@@ -19,8 +19,10 @@
 //     activation dword.  For the MFMA path, lane (row, qd) holds dword c,
 //     whose four fields cover columns 64c + 16qd + [0, 16): a 16x16x64 MFMA
 //     takes chunk c of 16 rows and its B operand is 16 contiguous bytes of q.
-//   scales: fp16 [tile][g8][row 0..63][8]: the scale of group g of a row is
-//     entry g % 8 of slot g / 8 (groups padded to a multiple of 8 with 0).
+//   scales: uint32 [tile][sc][row 0..63]: the fp16 scales of groups 2 sc (low
+//     half) and 2 sc + 1 (high half) of the row.  A wave with one row per lane
+//     reads a superchunk's scales as one 256-byte request; the MFMA path reads
+//     the pairs of four consecutive rows as one 16-byte load.
 //
 // ptq1_0 repacked (1.75 bits per weight kept, bytes only reordered)
 //   codes: uint4 [tile][sb][L 0..12][row 0..63], sb = superblock of 8 groups.
@@ -28,7 +30,8 @@
 //     bytes: D = 6*gi + m (gi < 8, m < 6) holds bytes 4m..4m+3 of group gi;
 //     D = 48 + p (p < 4) holds bytes 24, 25 of group 2p, then bytes 24, 25 of
 //     group 2p+1.  Bytes are copied unchanged (padding trits included).
-//   scales: as for pq2_0.
+//   scales: fp16 [tile][sb][row 0..63][8]: the scale of group g of a row is
+//     entry g % 8 of slot g / 8 (groups padded to a multiple of 8 with 0).
 #pragma once
 #include <stdint.h>
 
@@ -62,6 +65,7 @@ inline Dims dims(int64_t rows, int64_t cols) {
 // Byte sizes and offsets of the repacked buffers.
 inline int64_t pq2_code_bytes(const Dims& d) { return d.ntiles * d.nsc * 4 * 64 * 16; }
 inline int64_t ptq1_code_bytes(const Dims& d) { return d.ntiles * d.G8 * kPtqLoads * 64 * 16; }
-inline int64_t scale_bytes(const Dims& d) { return d.ntiles * d.G8 * 64 * 8 * 2; }
+inline int64_t pq2_scale_bytes(const Dims& d) { return d.ntiles * d.nsc * 64 * 4; }
+inline int64_t ptq1_scale_bytes(const Dims& d) { return d.ntiles * d.G8 * 64 * 8 * 2; }
 
 }  // namespace tq

@@ -63,7 +63,7 @@ int64_t tq_canonical_bytes(int fmt, int64_t rows, int64_t cols) {
 int64_t tq_repacked_bytes(int fmt, int64_t rows, int64_t cols) {
   if (shape_status(fmt, rows, cols, 1) != TQ_OK) return 0;
   const tq::Dims dm = tq::dims(rows, cols);
-  return (fmt == TQ_FMT_PQ2_0 ? tq::pq2_code_bytes(dm) : tq::ptq1_code_bytes(dm)) + tq::scale_bytes(dm);
+  return fmt == TQ_FMT_PQ2_0 ? tq::pq2_code_bytes(dm) + tq::pq2_scale_bytes(dm) : tq::ptq1_code_bytes(dm) + tq::ptq1_scale_bytes(dm);
 }
 
 int tq_repack(int fmt, const void* src, void* dst, int64_t rows, int64_t cols, int32_t* bad_flag, void* stream) {
@@ -98,22 +98,29 @@ int tq_quantize_q8k(const float* x, int64_t tokens, int64_t cols, int8_t* q, flo
   return hip_status(tq::launch_quantize_q8k(x, tokens * cols / 256, q, d, bsums, as_stream(stream)));
 }
 
+int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens) {
+  if (shape_status(fmt, rows, cols, tokens) != TQ_OK) return 0;
+  return tq::workspace_bytes(tq::dims(rows, cols));
+}
+
 int tq_gemv(int fmt, const void* w, int64_t rows, int64_t cols, const int8_t* q, const float* d, const int16_t* bsums,
-            float* y, void* stream) {
+            float* y, void* workspace, void* stream) {
   const int st = product_args(fmt, w, rows, cols, 1, q, d, bsums, y, true);
   if (st != TQ_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return TQ_ERR_ALIGN;
   const tq::Dims dm = tq::dims(rows, cols);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
-  if (fmt == TQ_FMT_PQ2_0) return hip_status(tq::launch_gemv_pq2(wb, dm, q, d, y, nullptr, as_stream(stream)));
-  return hip_status(tq::launch_gemv_ptq1(wb, dm, q, d, bsums, y, nullptr, as_stream(stream)));
+  if (fmt == TQ_FMT_PQ2_0) return hip_status(tq::launch_gemv_pq2(wb, dm, q, d, y, nullptr, workspace, as_stream(stream)));
+  return hip_status(tq::launch_gemv_ptq1(wb, dm, q, d, bsums, y, nullptr, workspace, as_stream(stream)));
 }
 
 int tq_gemm(int fmt, const void* w, int64_t rows, int64_t cols, int64_t tokens, const int8_t* q, const float* d,
-            const int16_t* bsums, float* y, void* stream) {
+            const int16_t* bsums, float* y, void* workspace, void* stream) {
   const int st = product_args(fmt, w, rows, cols, tokens, q, d, bsums, y, true);
   if (st != TQ_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return TQ_ERR_ALIGN;
   // A single token takes the matrix-vector kernel (page 1, "the leftovers").
-  if (tokens == 1) return tq_gemv(fmt, w, rows, cols, q, d, bsums, y, stream);
+  if (tokens == 1) return tq_gemv(fmt, w, rows, cols, q, d, bsums, y, workspace, stream);
   if (fmt != TQ_FMT_PQ2_0) return TQ_ERR_UNSUPPORTED;
   const tq::Dims dm = tq::dims(rows, cols);
   return hip_status(
@@ -127,8 +134,9 @@ int tq_group_dots(int fmt, const void* w, int64_t rows, int64_t cols, int64_t to
   const tq::Dims dm = tq::dims(rows, cols);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   if (tokens == 1) {
-    if (fmt == TQ_FMT_PQ2_0) return hip_status(tq::launch_gemv_pq2(wb, dm, q, nullptr, nullptr, idots, as_stream(stream)));
-    return hip_status(tq::launch_gemv_ptq1(wb, dm, q, nullptr, bsums, nullptr, idots, as_stream(stream)));
+    if (fmt == TQ_FMT_PQ2_0)
+      return hip_status(tq::launch_gemv_pq2(wb, dm, q, nullptr, nullptr, idots, nullptr, as_stream(stream)));
+    return hip_status(tq::launch_gemv_ptq1(wb, dm, q, nullptr, bsums, nullptr, idots, nullptr, as_stream(stream)));
   }
   if (fmt != TQ_FMT_PQ2_0) return TQ_ERR_UNSUPPORTED;
   return hip_status(tq::launch_gemm_pq2(wb, dm, tokens, q, nullptr, nullptr, idots, as_stream(stream)));

@@ -106,21 +106,36 @@ int tq_unrepack(int fmt, const void *src_repacked, void *dst, int64_t rows, int6
  * d == 0 gives q = 0 and bsums = 0.  Inputs must be finite. */
 int tq_quantize_q8k(const float *x, int64_t tokens, int64_t cols, int8_t *q, float *d, int16_t *bsums, void *stream);
 
+/* Bytes of the optional workspace of tq_gemv / tq_gemm for this shape.  The
+ * workspace lets a product split its columns over several workgroups per
+ * 64-row tile (fp64 partial sums plus per-tile arrival counters), which keeps
+ * all compute units busy when the row count is small and balances the load
+ * when it is large.  Contract: device memory of at least this size, 16-byte
+ * aligned, zero-filled once before its first use; every call leaves it zeroed
+ * again, so it can be reused by later calls (also inside a captured graph)
+ * without clearing.  Calls that run at the same time must not share one.
+ * Returns 0 for an invalid shape. */
+int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens);
+
 /* Matrix-vector product, one token (page 1, "the trick with 4 and 16" and
  * "did it reach the wall?"):
  *   y[r] = sum_g d_w[r][g] * d[g/2] * I[r][g],
  *   I[r][g] = sum_{k<128} w[r][128g+k] * q[128g+k]   (exact integer),
  * the float part evaluated in fp64 and rounded to fp32 once.  `w` is the
- * repacked matrix.  `bsums` is read for ptq1_0 and may be NULL for pq2_0. */
+ * repacked matrix.  `bsums` is read for ptq1_0 and may be NULL for pq2_0.
+ * `workspace` (nullable, see tq_workspace_bytes): without it each 64-row tile
+ * is one workgroup.  Results are deterministic either way; with and without a
+ * workspace they agree to within the fp64 rounding of the partial sums. */
 int tq_gemv(int fmt, const void *w, int64_t rows, int64_t cols, const int8_t *q, const float *d, const int16_t *bsums,
-            float *y, void *stream);
+            float *y, void *workspace, void *stream);
 
 /* Matrix product with a small batch of tokens (page 1, "prefill wants a
  * different shape" and "the leftovers"): y[t][r] for t < tokens, the same
  * arithmetic as tq_gemv per token.  Token counts that are not a multiple of
- * the kernel's tile are padded internally; padded outputs are never written. */
+ * the kernel's tile are padded internally; padded outputs are never written.
+ * A single token runs the matrix-vector kernel.  `workspace` as for tq_gemv. */
 int tq_gemm(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q, const float *d,
-            const int16_t *bsums, float *y, void *stream);
+            const int16_t *bsums, float *y, void *workspace, void *stream);
 
 /* Test export: the exact integer group dots I[t][r][g] (int32,
  * [tokens][rows][cols/128]) computed by the same kernels as tq_gemv

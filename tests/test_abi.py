@@ -41,7 +41,7 @@ def test_sizes(tq):
     assert tq.canonical_bytes("pq2_0", 17408, 5120) == 23674880
     assert tq.repacked_bytes("pq2_0", 17408, 5120) == 23674880
     # padding of the row tile (rows -> multiple of 64) and of ptq1_0 groups (-> multiple of 8)
-    assert tq.repacked_bytes("pq2_0", 1, 256) == 64 * 256 / 4 + 64 * 8 * 2  # codes + scales padded to 8 groups
+    assert tq.repacked_bytes("pq2_0", 1, 256) == 64 * 256 / 4 + 64 * 4  # codes + one scale pair per row and superchunk
     assert tq.repacked_bytes("ptq1_0", 65, 256) == 2 * 8 * 64 * 28
     assert tq.canonical_bytes("pq2_0", 0, 256) == 0
     assert tq.repacked_bytes(7, 64, 256) == 0
@@ -76,27 +76,29 @@ def test_validation_errors_touch_nothing(tq):
     good = P(0x100000)  # never dereferenced: each call below fails validation first
     odd = P(0x100001)
     # null pointers
-    assert L.tq_gemv(1, None, 64, 256, good, good, None, good, None) == tq.ERR_NULL
-    assert L.tq_gemv(1, good, 64, 256, good, None, None, good, None) == tq.ERR_NULL
-    assert L.tq_gemv(2, good, 64, 256, good, good, None, good, None) == tq.ERR_NULL  # ptq1_0 needs bsums
-    assert L.tq_gemm(1, good, 64, 256, 4, None, good, None, good, None) == tq.ERR_NULL
+    assert L.tq_gemv(1, None, 64, 256, good, good, None, good, None, None) == tq.ERR_NULL
+    assert L.tq_gemv(1, good, 64, 256, good, None, None, good, None, None) == tq.ERR_NULL
+    assert L.tq_gemv(2, good, 64, 256, good, good, None, good, None, None) == tq.ERR_NULL  # ptq1_0 needs bsums
+    assert L.tq_gemm(1, good, 64, 256, 4, None, good, None, good, None, None) == tq.ERR_NULL
     assert L.tq_quantize_q8k(None, 1, 256, good, good, good, None) == tq.ERR_NULL
     assert L.tq_repack(1, None, good, 64, 256, None, None) == tq.ERR_NULL
     assert L.tq_group_dots(1, good, 64, 256, 1, good, None, None, None) == tq.ERR_NULL
     # alignment
-    assert L.tq_gemv(1, odd, 64, 256, good, good, None, good, None) == tq.ERR_ALIGN
-    assert L.tq_gemv(1, good, 64, 256, odd, good, None, good, None) == tq.ERR_ALIGN
-    assert L.tq_gemv(1, good, 64, 256, good, odd, None, good, None) == tq.ERR_ALIGN
-    assert L.tq_gemv(1, good, 64, 256, good, good, None, P(0x100002), None) == tq.ERR_ALIGN
-    assert L.tq_gemv(2, good, 64, 256, good, good, odd, good, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, odd, 64, 256, good, good, None, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, odd, good, None, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, good, odd, None, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(1, good, 64, 256, good, good, None, P(0x100002), None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(2, good, 64, 256, good, good, odd, good, None, None) == tq.ERR_ALIGN
     assert L.tq_quantize_q8k(P(0x100004), 1, 256, good, good, good, None) == tq.ERR_ALIGN
     assert L.tq_repack(1, good, P(0x100008), 64, 256, None, None) == tq.ERR_ALIGN
     # shapes and formats
-    assert L.tq_gemv(1, good, 64, 200, good, good, None, good, None) == tq.ERR_SHAPE
-    assert L.tq_gemm(1, good, 64, 256, 0, good, good, None, good, None) == tq.ERR_SHAPE
+    assert L.tq_gemv(1, good, 64, 200, good, good, None, good, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemm(1, good, 64, 256, 0, good, good, None, good, None, None) == tq.ERR_SHAPE
     assert L.tq_quantize_q8k(good, 1, 100, good, good, good, None) == tq.ERR_SHAPE
-    assert L.tq_gemv(9, good, 64, 256, good, good, None, good, None) == tq.ERR_FORMAT
+    assert L.tq_gemv(9, good, 64, 256, good, good, None, good, None, None) == tq.ERR_FORMAT
     assert L.tq_unrepack(9, good, good, 64, 256, None) == tq.ERR_FORMAT
+    assert L.tq_gemv(1, good, 64, 256, good, good, None, good, P(0x100008), None) == tq.ERR_ALIGN  # workspace
+    assert L.tq_workspace_bytes(1, 64, 200, 1) == 0 and L.tq_workspace_bytes(1, 640, 8192, 1) > 0
     assert L.tq_last_hip_error() == 0
 
 
