@@ -12,10 +12,10 @@ resident in HBM; eight repacked copies (570 MB) are rotated so that the
 Prints ONE JSON line.  `value` is Gweights/s of the whole timed region (K
 steps captured in one HIP graph and replayed once, bracketed by
 synchronizations).  `roofline` is the matrix-vector kernel's algorithmic HBM
-bytes per launch divided by its mean duration, measured with HIP events
-around every launch of a second, eager pass of K steps on the same stream.
-`extra` carries the prompt-product (17408 x 5120, 4 and 64 tokens) and
-ptq1_0 figures; `cpu_baseline` times the CPU oracle on the host.
+bytes per launch divided by its mean duration, measured with one HIP event
+pair around K back-to-back launches of that kernel on the stream it runs on.
+`extra` carries the prompt-product (17408 x 5120, 4 and 64 tokens), 64-layer
+step and ptq1_0 figures; `cpu_baseline` times the CPU oracle on the host.
 """
 from __future__ import annotations
 
@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip the prompt-product and ptq1_0 figures")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="wall budget of the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the CPU baseline")
     return ap.parse_args()
 
 
@@ -58,22 +58,17 @@ def copies_for(nbytes: int) -> int:
     return max(2, -(-2 * MALL_BYTES // nbytes))
 
 
-class Timed:
-    """Per-launch HIP events on the current stream."""
-
-    def __init__(self, torch, n):
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        self.i = 0
-
-    def around(self, fn):
-        a, b = self.ev[self.i]
-        a.record()
-        fn()
-        b.record()
-        self.i += 1
-
-    def mean_us(self):
-        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in self.ev[: self.i]]))
+def batch_us(torch, call, K):
+    """Mean duration of K back-to-back launches of call(i) on the current
+    stream: one HIP event pair around the whole batch (no host gaps between
+    the kernels, so this is the kernels' own average as a tracer sees it)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / K
 
 
 def graph_time(torch, step, K):
@@ -111,27 +106,27 @@ def decode_bench(torch, tq, K, W):
     bs = torch.empty((1, C // 16), dtype=torch.int16, device="cuda")
     y = torch.empty(R, dtype=torch.float32, device="cuda")
 
-    def step(i, timer=None):
+    def step(i):
         tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs))
-        call = lambda: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
-        call() if timer is None else timer.around(call)
+        tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
-    # eager pass with per-launch events (roofline of the matrix-vector kernel)
-    timer = Timed(torch, K)
+    # eager pass of whole steps (host-launched, for reference)
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, timer)
+        step(i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
-    gemv_us = timer.mean_us()
+    # the matrix-vector kernel alone, K launches back to back on this stream
+    gemv_us = batch_us(torch, lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y), K)
+    quant_us = batch_us(torch, lambda i: tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs)), K)
     # graph pass: the timed region of `value`
     graph_s = graph_time(torch, step, K)
     algo_bytes = tq.repacked_bytes(fmt, R, C) + C + 4 * (C // 256) + 4 * R
     return {
-        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "eager_s": eager_s, "gemv_us": gemv_us,
+        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "eager_s": eager_s, "gemv_us": gemv_us, "quant_us": quant_us,
         "algo_bytes": algo_bytes, "weight_bytes": tq.repacked_bytes(fmt, R, C),
     }
 
@@ -146,15 +141,12 @@ def prefill_bench(torch, tq, T, K):
     del wdev
     q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
     y = torch.empty((T, R), dtype=torch.float32, device="cuda")
-    call = lambda i: tq.gemm(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+    ws = tq.workspace(fmt, R, C, T)
+    call = lambda i: tq.gemm(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y, ws=ws)
     for i in range(20):
         call(i)
     torch.cuda.synchronize()
-    timer = Timed(torch, K)
-    for i in range(K):
-        timer.around(lambda: call(i))
-    torch.cuda.synchronize()
-    us = timer.mean_us()
+    us = batch_us(torch, call, K)
     macs = R * C * T
     return {"tokens": T, "us": us, "gmac_s": macs / us / 1e3, "mfma_frac": 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12),
             "hbm_gbs": (tq.repacked_bytes(fmt, R, C) + T * C + 4 * T * (C // 256) + 4 * T * R) / us / 1e3}
@@ -170,17 +162,67 @@ def ptq1_bench(torch, tq, K):
     del wdev
     q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
     y = torch.empty(R, dtype=torch.float32, device="cuda")
-    call = lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+    ws = tq.workspace(fmt, R, C, 1)
+    call = lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y, ws=ws)
     for i in range(20):
         call(i)
     torch.cuda.synchronize()
-    timer = Timed(torch, K)
-    for i in range(K):
-        timer.around(lambda: call(i))
-    torch.cuda.synchronize()
-    us = timer.mean_us()
+    us = batch_us(torch, call, K)
     wb = tq.repacked_bytes(fmt, R, C)
     return {"us": us, "gweights_s": R * C / us / 1e3, "weight_gbs": wb / us / 1e3, "hbm_frac": wb / us / 1e3 / HBM_PEAK_GBS}
+
+
+def synth_pq2_gpu(torch, gen, rows, cols):
+    """Canonical pq2_0 blocks drawn on the device from a seeded generator
+    (timing does not depend on the values): each code byte is one of the 81
+    bytes whose four 2-bit fields are all valid, each scale uniform in
+    [0.01, 0.05] rounded to fp16, blocks laid out as fp16 d then 32 code bytes."""
+    G = cols // 128
+    table = torch.from_numpy(TI.VALID_PQ2_BYTES.astype(np.uint8)).cuda()
+    idx = torch.randint(0, table.numel(), (rows, G, 32), device="cuda", generator=gen)
+    codes = table[idx]
+    del idx
+    d = (torch.rand((rows, G), device="cuda", generator=gen) * 0.04 + 0.01).half()
+    return torch.cat([d.view(torch.uint8).view(rows, G, 2), codes], dim=2).reshape(-1)
+
+
+def step64_bench(torch, tq, reps):
+    """The 64-layer decode step for one token: for each layer the gate, up,
+    down, qkv and out matrices (distinct weights, 5.7 GB in all), each
+    preceded by a fresh q8_K quantization of its own N(0,1) activation vector.
+    The 320 quantize + matrix-vector pairs are captured in one graph."""
+    fmt = "pq2_0"
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(TI.SEED_BASE + TI.STEP64)
+    mats = []
+    for layer in range(64):
+        for _name, R, C in TI.STEP64_SHAPES:
+            canon = synth_pq2_gpu(torch, gen, R, C)
+            mats.append((R, C, tq.repack(canon, fmt, R, C, check_codes=False)))
+            del canon
+    kmax = max(C for _, C, _ in mats)
+    rmax = max(R for R, _, _ in mats)
+    xs = torch.randn((len(mats), kmax), device="cuda", generator=gen)
+    q = torch.empty(kmax, dtype=torch.int8, device="cuda")
+    d = torch.empty(kmax // 256, dtype=torch.float32, device="cuda")
+    bs = torch.empty(kmax // 16, dtype=torch.int16, device="cuda")
+    y = torch.empty(rmax, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(tq.workspace_bytes(fmt, R, C) for R, C, _ in mats), dtype=torch.uint8, device="cuda")
+
+    def step(_i):
+        for m, (R, C, Wd) in enumerate(mats):
+            tq.quantize_q8k(xs[m, :C].view(1, C), out=(q[:C].view(1, C), d[: C // 256].view(1, -1), bs[: C // 16].view(1, -1)))
+            tq.gemv(fmt, Wd, R, C, q[:C], d[: C // 256], bs[: C // 16], out=y[:R], ws=ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    g_s = graph_time(torch, step, reps)
+    weights = sum(R * C for R, C, _ in mats)
+    wbytes = sum(tq.repacked_bytes(fmt, R, C) for R, C, _ in mats)
+    ms = g_s * 1e3 / reps
+    return {"matrices": len(mats), "ms_per_token": ms, "gweights_s": weights / (ms * 1e-3) / 1e9,
+            "weight_gbs": wbytes / (ms * 1e-3) / 1e9, "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "weight_bytes": wbytes}
 
 
 def quantize_bench(torch, tq, K):
@@ -190,11 +232,9 @@ def quantize_bench(torch, tq, K):
            torch.empty((1, 512), dtype=torch.int16, device="cuda"))
     for _ in range(20):
         tq.quantize_q8k(xs, out=out)
-    timer = Timed(torch, K)
-    for _ in range(K):
-        timer.around(lambda: tq.quantize_q8k(xs, out=out))
     torch.cuda.synchronize()
-    return {"cols": C, "us": timer.mean_us()}
+    us = batch_us(torch, lambda i: tq.quantize_q8k(xs, out=out), K)
+    return {"cols": C, "us": us}
 
 
 def ceiling_probe(torch):
@@ -291,6 +331,8 @@ def main():
         for T in (4, 64):
             p = prefill_bench(torch, tq, T, 200)
             extra[f"prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
+        log("64-layer step")
+        extra["step64"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in step64_bench(torch, tq, 5).items()}
         p = ptq1_bench(torch, tq, 200)
         extra["ptq1_decode"] = {k: round(v, 4) for k, v in p.items()}
         extra["quantize_8192"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in quantize_bench(torch, tq, 200).items()}
