@@ -25,6 +25,9 @@ FLAGS = [
     "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source extras: the MFMA kernel keeps its accumulators in ordinary VGPRs,
+# so the epilogue reads them without v_accvgpr_read copies.
+EXTRA = {"k_gemm_pq2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, out: str, extra=()) -> None:
@@ -42,7 +45,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory() as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
         with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
-            list(ex.map(lambda a: _compile(*a), zip(SOURCES, objs)))
+            list(ex.map(lambda a: _compile(a[0], a[1], EXTRA.get(a[0], ())), zip(SOURCES, objs)))
         tmp_lib = LIB + ".tmp"
         subprocess.check_call([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
