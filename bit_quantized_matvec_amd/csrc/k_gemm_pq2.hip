@@ -103,11 +103,16 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
 
   v4u ra[D], rs[D], rbv[D][BPT];
   float rx[D];
+  // Fetches past the last superchunk read cache-resident activation bytes in
+  // place of codes and scales (no HBM traffic); every load stays
+  // unconditional so that the wait counts stay exact.
+  const v4u* dummy = reinterpret_cast<const v4u*>(q) + (tid & 15);
 #define TQ_FETCH(J, SC)                                                                  \
   {                                                                                      \
-    const int scf = min((SC), nsc - 1); /* past the end: reload the last one (unused) */ \
-    ra[J] = __builtin_nontemporal_load(a_src + (size_t)scf * 256);                       \
-    rs[J] = s_src[(size_t)scf * 16];                                                     \
+    const bool real = (SC) < nsc;                                                        \
+    const int scf = min((SC), nsc - 1);                                                  \
+    ra[J] = __builtin_nontemporal_load(real ? a_src + (size_t)scf * 256 : dummy);        \
+    rs[J] = *(real ? s_src + (size_t)scf * 16 : dummy);                                  \
     _Pragma("unroll") for (int k = 0; k < BPT; ++k) rbv[J][k] =                          \
         *reinterpret_cast<const v4u*>(b_src[k] + (size_t)scf * 256);                     \
     rx[J] = x_src[scf];                                                                  \

@@ -10,7 +10,8 @@
 //   * one lane = one row; a workgroup = one 64-row tile and one slice of the
 //     columns; its waves split the slice into runs of 256-column superchunks;
 //   * per superchunk a lane issues four non-temporal dwordx4 loads (qd = 0..3),
-//     each a fully coalesced 1 KiB wave request (the codes are never reused);
+//     each a fully coalesced 1 KiB wave request (the codes are never reused),
+//     plus its row's scale pair, two superchunks ahead of their use;
 //   * the activation bytes a lane needs are the same for every lane of the
 //     wave, so they come in with scalar loads and feed v_dot4_i32_i8 from
 //     SGPRs -- no LDS traffic, no VGPRs;
@@ -32,18 +33,16 @@ namespace tq {
 namespace {
 
 constexpr int kMaxWaves = 16;
+constexpr size_t kMaxStageBytes = 32 * 1024;  // LDS for one slice's staged activations
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Weight codes are read once and never reused: non-temporal loads keep them
 // from displacing reusable lines and stream measurably faster on gfx950.
 template <bool NT>
-__device__ __forceinline__ uint4 load_codes(const uint4* p) {
-  if (NT) {
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return uint4{t.x, t.y, t.z, t.w};
-  }
-  return *p;
+__device__ __forceinline__ v4u load_codes(const uint4* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return *reinterpret_cast<const v4u*>(p);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -58,10 +57,10 @@ __device__ __forceinline__ int slot64(uint32_t d, int s) {
 // Integer dots of one superchunk: i0 for group 2 sc (dwords c = 0, 1), i1 for
 // group 2 sc + 1 (c = 2, 3).  `a` points at the superchunk's 64 activation
 // dwords (wave-uniform).
-__device__ __forceinline__ void superchunk_dots(const uint4 (&v)[4], const int* __restrict__ a, int& i0, int& i1) {
+__device__ __forceinline__ void superchunk_dots(const v4u (&v)[4], const int* __restrict__ a, int& i0, int& i1) {
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
-    const uint32_t dw[4] = {v[qd].x, v[qd].y, v[qd].z, v[qd].w};
+    const uint32_t dw[4] = {v[qd][0], v[qd][1], v[qd][2], v[qd][3]};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -80,7 +79,7 @@ __device__ __forceinline__ void superchunk_dots(const uint4 (&v)[4], const int* 
 
 // grid = (ntiles, slices).  Workgroup (tile, slice) covers superchunks
 // [slice * scw, min(nsc, (slice + 1) * scw)); its waves take runs of spw.
-template <int UNROLL, bool IDOTS, bool NT>
+template <int RING, bool IDOTS, bool NT, bool LDSQ>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* __restrict__ codes,
                                                                   const uint32_t* __restrict__ scales,
                                                                   const int* __restrict__ q, const float* __restrict__ dx,
@@ -105,7 +104,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
   const uint32_t* sp = scales + (size_t)tile * nsc * 64 + lane;
   double acc = 0.0;
 
-  auto epilogue = [&](int sc, int i0, int i1) {
+  // The activations were typically written by the previous kernel, so every
+  // line of them misses in this XCD's caches.  Read where they are used (one
+  // scalar load per superchunk), those misses would serialize behind each
+  // superchunk (measured: +6 us on 32768 x 8192 after the quantizer); instead
+  // the workgroup first copies its slice's q into LDS with wide vector loads,
+  // one burst, and the products read it from there.  (d_x, one cache line per
+  // slice, stays a scalar load.)
+  extern __shared__ int stage[];  // LDSQ: (wg1 - wg0) * 64 activation dwords
+  const int* qa = q + (size_t)wg0 * 64;  // activations of the slice, indexed by sc - wg0
+  if (LDSQ) {
+    const int nd = (wg1 - wg0) * 64;
+    for (int i = threadIdx.x * 4; i < nd; i += blockDim.x * 4)
+      *reinterpret_cast<uint4*>(&stage[i]) = *reinterpret_cast<const uint4*>(&qa[i]);
+    __syncthreads();
+    qa = stage;
+  }
+
+  auto epilogue = [&](int sc, int i0, int i1, uint32_t s2) {
     const int I0 = i0 >> 6, I1 = i1 >> 6;  // exact: both are 64 * I
     if (IDOTS) {
       if (row < rows) {
@@ -113,35 +129,53 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
         idots[(size_t)row * G + 2 * sc + 1] = I1;
       }
     } else {
-      const uint32_t s2 = sp[sc * 64];  // fp16 scales of groups 2sc, 2sc+1
+      // s2: fp16 scales of groups 2sc (low half) and 2sc+1
       const double dxs = (double)dx[sc];
       acc += ((double)half_bits_to_float(s2 & 0xffffu) * dxs) * (double)I0;
       acc += ((double)half_bits_to_float(s2 >> 16) * dxs) * (double)I1;
     }
   };
 
-  int sc = sc0;
-  for (; sc + UNROLL <= sc1; sc += UNROLL) {
-    uint4 v[UNROLL][4];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) v[u][qd] = load_codes<NT>(cp + (size_t)((sc + u) * 4 + qd) * 64);
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      int i0 = 0, i1 = 0;
-      superchunk_dots(v[u], q + (size_t)(sc + u) * 64, i0, i1);
-      epilogue(sc + u, i0, i1);
-    }
+  // The wave's superchunks [sc0, sc1) stream through a ring of RD slots: the
+  // codes and the scale pair of superchunk j + RD are fetched while j is
+  // multiplied.  The first pass only fetches, so the state at the loop header
+  // is the steady state and the compiler's wait counts stay exact.  Two slots (8 KiB
+  // in flight per wave) measured fastest: deeper rings put more requests in
+  // flight per CU than HBM serves better.
+  constexpr int RD = RING;
+  static_assert(RD == 2, "the passes below are written out for two slots");
+  const int n = sc1 - sc0;
+  v4u rc[RD][4];
+  uint32_t rsc[RD];
+  // Fetches past the end of the run read 256 bytes of the (cache-resident)
+  // activation vector instead of reloading codes from HBM; the loads stay
+  // unconditional so that the wait counts stay exact.
+  const uint4* dummy_c = reinterpret_cast<const uint4*>(q) + (lane & 15);
+  const uint32_t* dummy_s = reinterpret_cast<const uint32_t*>(q) + lane;
+#define TQ_FETCH(J, K)                                                                                   \
+  {                                                                                                      \
+    const bool real = (K) < n;                                                                           \
+    const int scf = sc0 + max(min((K), n - 1), 0);                                                       \
+    const uint4* c0 = real ? cp + (size_t)scf * 256 : dummy_c;                                           \
+    const uint32_t* s0 = real ? sp + (size_t)scf * 64 : dummy_s;                                         \
+    _Pragma("unroll") for (int qd = 0; qd < 4; ++qd) rc[J][qd] = load_codes<NT>(c0 + (real ? qd * 64 : 0)); \
+    rsc[J] = *s0;                                                                                        \
   }
-  for (; sc < sc1; ++sc) {
-    uint4 v[4];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) v[qd] = load_codes<NT>(cp + (size_t)(sc * 4 + qd) * 64);
-    int i0 = 0, i1 = 0;
-    superchunk_dots(v, q + (size_t)sc * 64, i0, i1);
-    epilogue(sc, i0, i1);
+#define TQ_STEP(J)                                                                                       \
+  {                                                                                                      \
+    const int j = base + J;                                                                              \
+    if (j >= 0 && j < n) {                                                                               \
+      int i0 = 0, i1 = 0;                                                                                \
+      superchunk_dots(rc[J], qa + (size_t)(sc0 + j - wg0) * 64, i0, i1);                                 \
+      epilogue(sc0 + j, i0, i1, rsc[J]);                                                                 \
+    }                                                                                                    \
+    TQ_FETCH(J, j + RD)                                                                                  \
   }
+  for (int base = -RD; base < n; base += RD) {
+    TQ_STEP(0) TQ_STEP(1)
+  }
+#undef TQ_STEP
+#undef TQ_FETCH
 
   if (IDOTS) return;
   red[wave][lane] = acc;
@@ -197,7 +231,7 @@ GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace) {
 
 hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
                                 int32_t* idots, void* workspace, const GemvPlan& p, hipStream_t s) {
-  constexpr int kUnroll = 2;
+  constexpr int kRing = 2;
   const int nsc = (int)dm.nsc;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
@@ -205,14 +239,21 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   double* partials =
       workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
-  if (idots)
-    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, true, true>), grid, block, 0, s, codes, scales,
-                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, p.scw, p.spw,
-                       partials, counters);
-  else
-    hipLaunchKernelGGL((gemv_pq2_kernel<kUnroll, false, true>), grid, block, 0, s, codes, scales,
-                       reinterpret_cast<const int*>(q), dx, y, idots, (int)dm.rows, nsc, (int)dm.G8, p.scw, p.spw,
-                       partials, counters);
+  // one slice's activations are staged in LDS when they fit (always with the
+  // column splits a workspace allows for matrices of up to 128 Ki columns)
+  const size_t stage = (size_t)p.scw * 256;
+  const bool ldsq = stage <= kMaxStageBytes;
+  const int* qi = reinterpret_cast<const int*>(q);
+  const int ns = (int)dm.G8;
+#define TQ_LAUNCH(ID, LQ)                                                                                     \
+  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ>), grid, block, LQ ? (unsigned)stage : 0u, s, codes, \
+                     scales, qi, dx, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
+  if (idots) {
+    if (ldsq) TQ_LAUNCH(true, true); else TQ_LAUNCH(true, false);
+  } else {
+    if (ldsq) TQ_LAUNCH(false, true); else TQ_LAUNCH(false, false);
+  }
+#undef TQ_LAUNCH
   return hipGetLastError();
 }
 
