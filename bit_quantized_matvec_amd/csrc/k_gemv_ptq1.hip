@@ -11,8 +11,9 @@
 //     superblock (1.75 bits per weight, bytes only reordered by the repack);
 //   * the four bytes of a code dword are split into two pairs of 16-bit lanes
 //     (bytes 0, 2 and bytes 1, 3), so one 32-bit multiply-by-3 advances two
-//     bytes at once without carries between them; each step yields a dword of
-//     four trits (one per byte) = one dot4 operand;
+//     bytes at once without carries between them; after it the high byte of
+//     each lane is that byte's trit, and one v_perm_b32 gathers the four into
+//     a dword = one dot4 operand;
 //   * the trits are w + 1, so I = dot(t, q) - sum(q), the group sum coming
 //     from the q8_K partial sums (page 1, "the trick with 4 and 16": sum(y)
 //     over 128 values is one add over 8 partial sums);
@@ -134,7 +135,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
         for (int j = 0; j < 5; ++j) {
           e *= 3u;
           o *= 3u;
-          const int t = (int)(((e >> 8) & 0x00030003u) | (o & 0x03000300u));
+          // each 16-bit lane now holds 3v < 768, so its high byte is the trit:
+          // one byte permute gathers the four (bytes 1, 3 of e and of o)
+          const int t = (int)__builtin_amdgcn_perm(o, e, 0x07030501u);
           if (m < 6) {
             ia = __builtin_amdgcn_sdot4(t, (int)tv[j], ia, false);
           } else if (m < 12) {
