@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the prompt-product and ptq1_0 figures")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the CPU baseline")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run 20 decode matrix-vector launches and three 1 GiB device copies "
+                         "(the workload of the FETCH_SIZE / WRITE_SIZE counter runs), print nothing")
     return ap.parse_args()
 
 
@@ -263,6 +266,50 @@ def ceiling_probe(torch):
     return {"read_sum_2GiB_gbs": read_gbs, "copy_1GiB_gbs": copy_gbs}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_32768x8192.json")
+GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", "k_gemv_pq2.hip")
+
+
+def traffic_probe(torch, tq):
+    """The workload of the HBM-traffic counter runs: 20 launches of the
+    decode matrix-vector kernel (rotating weight copies, as in the timed
+    run) and three device-to-device copies of 1 GiB, whose known byte count
+    calibrates the counters."""
+    fmt, Wc, x = TI.make("decode_32768x8192")
+    R, G, _ = Wc.shape
+    C = G * 128
+    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
+    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
+    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
+    del wdev
+    q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+    for i in range(20):
+        tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+    torch.cuda.synchronize()
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty(n, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter
+    runs, or None if the kernel source changed since they were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(GEMV_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle on the host cores: quantize + product over the full
     32768 x 8192 matrix, repeated while the wall budget lasts."""
@@ -299,6 +346,9 @@ def main():
         sys.exit(2)
     import bit_quantized_matvec_amd as tq
 
+    if args.traffic_probe:
+        traffic_probe(torch, tq)
+        return
     log("decode bench")
     dec = decode_bench(torch, tq, args.steps, args.warmup)
     R, C, K = dec["R"], dec["C"], args.steps
@@ -320,7 +370,7 @@ def main():
         "config": {"workload": "decode_32768x8192", "format": "pq2_0", "rows": R, "cols": C, "tokens": 1,
                    "step": "tq_quantize_q8k + tq_gemv", "weight_copies_rotated": dec["copies"], "timing": "hip graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "gemv_pq2_kernel", "kernel_us": round(dec["gemv_us"], 3), "algo_bytes": dec["algo_bytes"]},
     }
     extra = {"decode_eager_gweights_s": round(K * R * C / dec["eager_s"] / 1e9, 2),
