@@ -109,11 +109,16 @@ def decode_bench(torch, tq, K, W):
     bs = torch.empty((1, C // 16), dtype=torch.int16, device="cuda")
     y = torch.empty(R, dtype=torch.float32, device="cuda")
 
-    def step(i):
+    def step_two(i):
         tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs))
         tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
 
+    def step(i):
+        # one launch: every workgroup quantizes x itself, on chip
+        tq.gemv_f32(fmt, Ws[i % ncopy], R, C, xs[i % 64], out=y)
+
     for i in range(W):
+        step_two(i)
         step(i)
     torch.cuda.synchronize()
     # eager pass of whole steps (host-launched, for reference)
@@ -122,15 +127,20 @@ def decode_bench(torch, tq, K, W):
         step(i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
-    # the matrix-vector kernel alone, K launches back to back on this stream
+    # the product kernel alone, K launches back to back on this stream
+    fused_us = batch_us(torch, step, K)
     gemv_us = batch_us(torch, lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y), K)
     quant_us = batch_us(torch, lambda i: tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs)), K)
-    # graph pass: the timed region of `value`
+    # graph passes: the timed region of `value` (fused step), and the two-kernel step
     graph_s = graph_time(torch, step, K)
-    algo_bytes = tq.repacked_bytes(fmt, R, C) + C + 4 * (C // 256) + 4 * R
+    graph_two_s = graph_time(torch, step_two, K)
+    wbytes = tq.repacked_bytes(fmt, R, C)
     return {
-        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "eager_s": eager_s, "gemv_us": gemv_us, "quant_us": quant_us,
-        "algo_bytes": algo_bytes, "weight_bytes": tq.repacked_bytes(fmt, R, C),
+        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "graph_two_s": graph_two_s, "eager_s": eager_s,
+        "fused_us": fused_us, "gemv_us": gemv_us, "quant_us": quant_us,
+        # algorithmic bytes per launch: weights + fp32 x + fp32 y (fused); weights + q + d + y (two-kernel GEMV)
+        "algo_bytes": wbytes + 4 * C + 4 * R, "algo_bytes_gemv": wbytes + C + 4 * (C // 256) + 4 * R,
+        "weight_bytes": wbytes,
     }
 
 
@@ -212,20 +222,27 @@ def step64_bench(torch, tq, reps):
     y = torch.empty(rmax, dtype=torch.float32, device="cuda")
     ws = torch.zeros(max(tq.workspace_bytes(fmt, R, C) for R, C, _ in mats), dtype=torch.uint8, device="cuda")
 
-    def step(_i):
+    def step_two(_i):
         for m, (R, C, Wd) in enumerate(mats):
             tq.quantize_q8k(xs[m, :C].view(1, C), out=(q[:C].view(1, C), d[: C // 256].view(1, -1), bs[: C // 16].view(1, -1)))
             tq.gemv(fmt, Wd, R, C, q[:C], d[: C // 256], bs[: C // 16], out=y[:R], ws=ws)
 
+    def step(_i):
+        for m, (R, C, Wd) in enumerate(mats):
+            tq.gemv_f32(fmt, Wd, R, C, xs[m, :C], out=y[:R], ws=ws)
+
+    step_two(0)
     step(0)
     torch.cuda.synchronize()
     g_s = graph_time(torch, step, reps)
+    g2_s = graph_time(torch, step_two, reps)
     weights = sum(R * C for R, C, _ in mats)
     wbytes = sum(tq.repacked_bytes(fmt, R, C) for R, C, _ in mats)
     ms = g_s * 1e3 / reps
-    return {"matrices": len(mats), "ms_per_token": ms, "gweights_s": weights / (ms * 1e-3) / 1e9,
+    return {"matrices": len(mats), "step": "tq_gemv_f32 per matrix", "ms_per_token": ms,
+            "gweights_s": weights / (ms * 1e-3) / 1e9,
             "weight_gbs": wbytes / (ms * 1e-3) / 1e9, "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "weight_bytes": wbytes}
+            "weight_bytes": wbytes, "two_kernel_ms_per_token": g2_s * 1e3 / reps}
 
 
 def quantize_bench(torch, tq, K):
@@ -272,9 +289,10 @@ GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", "k_gemv_pq2
 
 def traffic_probe(torch, tq):
     """The workload of the HBM-traffic counter runs: 20 launches of the
-    decode matrix-vector kernel (rotating weight copies, as in the timed
-    run) and three device-to-device copies of 1 GiB, whose known byte count
-    calibrates the counters."""
+    decode product with quantization inside (the timed step), then 20 of the
+    matrix-vector kernel on a stored q8_K vector (rotating weight copies, as
+    in the timed run), and three device-to-device copies of 1 GiB, whose
+    known byte count calibrates the counters."""
     fmt, Wc, x = TI.make("decode_32768x8192")
     R, G, _ = Wc.shape
     C = G * 128
@@ -282,8 +300,11 @@ def traffic_probe(torch, tq):
     ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
     Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
     del wdev
-    q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+    xd = torch.from_numpy(x).cuda()
+    q, d, bs = tq.quantize_q8k(xd)
     y = torch.empty(R, dtype=torch.float32, device="cuda")
+    for i in range(20):
+        tq.gemv_f32(fmt, Ws[i % ncopy], R, C, xd[0], out=y)
     for i in range(20):
         tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
     torch.cuda.synchronize()
@@ -353,7 +374,7 @@ def main():
     dec = decode_bench(torch, tq, args.steps, args.warmup)
     R, C, K = dec["R"], dec["C"], args.steps
     value = K * R * C / dec["graph_s"] / 1e9
-    achieved = dec["algo_bytes"] / (dec["gemv_us"] * 1e-6) / 1e9
+    achieved = dec["algo_bytes"] / (dec["fused_us"] * 1e-6) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -368,14 +389,22 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "decode_32768x8192", "format": "pq2_0", "rows": R, "cols": C, "tokens": 1,
-                   "step": "tq_quantize_q8k + tq_gemv", "weight_copies_rotated": dec["copies"], "timing": "hip graph of K steps"},
+                   "step": "tq_gemv_f32 (q8_K quantization inside the product kernel)",
+                   "weight_copies_rotated": dec["copies"], "timing": "hip graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "gemv_pq2_kernel", "kernel_us": round(dec["gemv_us"], 3), "algo_bytes": dec["algo_bytes"]},
+                     "kernel": "gemv_pq2_kernel (fused q8_K)", "kernel_us": round(dec["fused_us"], 3),
+                     "algo_bytes": dec["algo_bytes"]},
     }
     extra = {"decode_eager_gweights_s": round(K * R * C / dec["eager_s"] / 1e9, 2),
-             "decode_weight_gbs": round(dec["weight_bytes"] / (dec["gemv_us"] * 1e-6) / 1e9, 1),
-             "decode_gemv_gweights_s": round(R * C / dec["gemv_us"] / 1e3, 1)}
+             "decode_two_kernel_step": {"step": "tq_quantize_q8k + tq_gemv",
+                                        "gweights_s": round(K * R * C / dec["graph_two_s"] / 1e9, 2),
+                                        "us_per_step": round(dec["graph_two_s"] * 1e6 / K, 3),
+                                        "gemv_us": round(dec["gemv_us"], 3), "quant_us": round(dec["quant_us"], 3),
+                                        "gemv_hbm_frac": round(dec["algo_bytes_gemv"] / (dec["gemv_us"] * 1e-6) / 1e9
+                                                               / HBM_PEAK_GBS, 4)},
+             "decode_weight_gbs": round(dec["weight_bytes"] / (dec["fused_us"] * 1e-6) / 1e9, 1),
+             "decode_kernel_gweights_s": round(R * C / dec["fused_us"] / 1e3, 1)}
     if not args.no_extra:
         log("prefill / ptq1 / quantize / ceiling")
         for T in (4, 64):

@@ -36,6 +36,7 @@ _SIGS = {
     "tq_quantize_q8k": ([_p, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_workspace_bytes": ([_i32, _i64, _i64, _i64], _i64),
     "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
+    "tq_gemv_f32": ([_i32, _p, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_group_dots": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_status_str": ([_i32], ctypes.c_char_p),
@@ -159,6 +160,17 @@ def gemv(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None,
         out = torch.empty(rows, dtype=torch.float32, device=w.device)
     _check(_lib.tq_gemv(_fmt(fmt), _ptr(w), rows, cols, _ptr(q), _ptr(d), _ptr(bsums), _ptr(out), _ptr(ws),
                         _stream()), "tq_gemv")
+    return out
+
+
+def gemv_f32(fmt, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, out=None, ws=None) -> torch.Tensor:
+    """y[rows] = W q8_K(x) for one fp32 token x [cols] or [1, cols], quantized
+    inside the product kernel (bit-identical to quantize_q8k followed by gemv)."""
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.numel() != cols:
+        raise TQError(ERR_SHAPE, "gemv_f32: x must be a contiguous float32 tensor of cols elements")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _check(_lib.tq_gemv_f32(_fmt(fmt), _ptr(w), rows, cols, _ptr(x), _ptr(out), _ptr(ws), _stream()), "tq_gemv_f32")
     return out
 
 

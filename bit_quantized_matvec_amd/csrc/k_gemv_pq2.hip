@@ -28,6 +28,7 @@
 //     The result is therefore deterministic, and no memset is needed between
 //     calls (safe inside a captured graph).
 #include "kernels.h"
+#include "q8k_block.h"
 
 namespace tq {
 namespace {
@@ -79,10 +80,14 @@ __device__ __forceinline__ void superchunk_dots(const v4u (&v)[4], const int* __
 
 // grid = (ntiles, slices).  Workgroup (tile, slice) covers superchunks
 // [slice * scw, min(nsc, (slice + 1) * scw)); its waves take runs of spw.
-template <int RING, bool IDOTS, bool NT, bool LDSQ>
+// FX: the activations come in as fp32 x (`xf`, `q` and `dx` unused) and each
+// workgroup quantizes its slice to q8_K itself, into LDS (requires LDSQ), in
+// batches of XB blocks per wave (XB at least the blocks per wave, up to 8).
+template <int RING, bool IDOTS, bool NT, bool LDSQ, bool FX, int XB = 1>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* __restrict__ codes,
                                                                   const uint32_t* __restrict__ scales,
                                                                   const int* __restrict__ q, const float* __restrict__ dx,
+                                                                  const float4* __restrict__ xf,
                                                                   float* __restrict__ y, int32_t* __restrict__ idots,
                                                                   int rows, int nsc, int G8, int scw, int spw,
                                                                   double* __restrict__ partials, unsigned* __restrict__ counters) {
@@ -108,18 +113,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
   // line of them misses in this XCD's caches.  Read where they are used (one
   // scalar load per superchunk), those misses would serialize behind each
   // superchunk (measured: +6 us on 32768 x 8192 after the quantizer); instead
-  // the workgroup first copies its slice's q into LDS with wide vector loads,
-  // one burst, and the products read it from there.  (d_x, one cache line per
-  // slice, stays a scalar load.)
-  extern __shared__ int stage[];  // LDSQ: (wg1 - wg0) * 64 activation dwords
+  // the workgroup first brings its slice's activations into LDS (a copy of q,
+  // or with FX its own q8_K of x), and the products read them from there.
+  static_assert(!FX || LDSQ, "the fused quantization writes its q8_K into the LDS stage");
+  extern __shared__ int stage[];  // LDSQ: nb * 64 activation dwords; FX: then nb d_x
+  const int nb = wg1 - wg0;       // superchunks of the slice (= q8_K blocks of 256 columns)
   const int* qa = q + (size_t)wg0 * 64;  // activations of the slice, indexed by sc - wg0
-  if (LDSQ) {
-    const int nd = (wg1 - wg0) * 64;
-    for (int i = threadIdx.x * 4; i < nd; i += blockDim.x * 4)
-      *reinterpret_cast<uint4*>(&stage[i]) = *reinterpret_cast<const uint4*>(&qa[i]);
-    __syncthreads();
-    qa = stage;
-  }
+  const float* xa = dx + wg0;            // d_x of the slice, indexed by sc - wg0
 
   auto epilogue = [&](int sc, int i0, int i1, uint32_t s2) {
     const int I0 = i0 >> 6, I1 = i1 >> 6;  // exact: both are 64 * I
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
       }
     } else {
       // s2: fp16 scales of groups 2sc (low half) and 2sc+1
-      const double dxs = (double)dx[sc];
+      const double dxs = (double)xa[sc - wg0];
       acc += ((double)half_bits_to_float(s2 & 0xffffu) * dxs) * (double)I0;
       acc += ((double)half_bits_to_float(s2 >> 16) * dxs) * (double)I1;
     }
@@ -138,10 +138,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
 
   // The wave's superchunks [sc0, sc1) stream through a ring of RD slots: the
   // codes and the scale pair of superchunk j + RD are fetched while j is
-  // multiplied.  The first pass only fetches, so the state at the loop header
-  // is the steady state and the compiler's wait counts stay exact.  Two slots (8 KiB
-  // in flight per wave) measured fastest: deeper rings put more requests in
-  // flight per CU than HBM serves better.
+  // multiplied.  The prologue fills the ring, so the state at the loop
+  // header is the steady state and the compiler's wait counts stay exact.
+  // Two slots (8 KiB in flight per wave) measured fastest: deeper rings put
+  // more requests in flight per CU than HBM serves better.
   constexpr int RD = RING;
   static_assert(RD == 2, "the passes below are written out for two slots");
   const int n = sc1 - sc0;
@@ -150,8 +150,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
   // Fetches past the end of the run read 256 bytes of the (cache-resident)
   // activation vector instead of reloading codes from HBM; the loads stay
   // unconditional so that the wait counts stay exact.
-  const uint4* dummy_c = reinterpret_cast<const uint4*>(q) + (lane & 15);
-  const uint32_t* dummy_s = reinterpret_cast<const uint32_t*>(q) + lane;
+  const void* hot = FX ? static_cast<const void*>(xf) : static_cast<const void*>(q);  // >= 256 cache-resident bytes
+  const uint4* dummy_c = static_cast<const uint4*>(hot) + (lane & 15);
+  const uint32_t* dummy_s = static_cast<const uint32_t*>(hot) + lane;
 #define TQ_FETCH(J, K)                                                                                   \
   {                                                                                                      \
     const bool real = (K) < n;                                                                           \
@@ -164,14 +165,65 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
 #define TQ_STEP(J)                                                                                       \
   {                                                                                                      \
     const int j = base + J;                                                                              \
-    if (j >= 0 && j < n) {                                                                               \
+    if (j < n) {                                                                                         \
       int i0 = 0, i1 = 0;                                                                                \
       superchunk_dots(rc[J], qa + (size_t)(sc0 + j - wg0) * 64, i0, i1);                                 \
       epilogue(sc0 + j, i0, i1, rsc[J]);                                                                 \
     }                                                                                                    \
     TQ_FETCH(J, j + RD)                                                                                  \
   }
-  for (int base = -RD; base < n; base += RD) {
+
+  // Prologue: the activation loads go out first and the ring's first fetches
+  // right behind them; staging then waits only for the activations (loads
+  // complete in order), so it overlaps the HBM latency of the codes.
+  if (FX) {
+    // q8_K of the slice, block b (one superchunk) by wave b mod nw, in batches
+    // of XB blocks per wave whose loads are all in flight together; the same
+    // arithmetic as the standalone quantizer (q8k_block.h).  A batch slot past
+    // the slice redoes the slice's last block and stores the same bits to the
+    // same place: no branch, so the compiler keeps the loads where they are.
+    constexpr int kXB = XB;
+    float* sd = reinterpret_cast<float*>(stage + nb * 64);
+    float4 v[kXB];
+    auto load_batch = [&](int b0) {
+#pragma unroll
+      for (int i = 0; i < kXB; ++i) v[i] = xf[(size_t)(wg0 + min(b0 + wave + i * nw, nb - 1)) * 64 + lane];
+    };
+    auto quant_batch = [&](int b0) {
+#pragma unroll
+      for (int i = 0; i < kXB; ++i) {
+        const int b = min(b0 + wave + i * nw, nb - 1);
+        const float db = q8k_block_scale(v[i]);
+        stage[b * 64 + lane] =
+            q8k_pack4(q8k_quant1(v[i].x, db), q8k_quant1(v[i].y, db), q8k_quant1(v[i].z, db), q8k_quant1(v[i].w, db));
+        if (lane == 0) sd[b] = db;
+      }
+    };
+    load_batch(0);
+    TQ_FETCH(0, 0)
+    TQ_FETCH(1, 1)
+    __builtin_amdgcn_sched_barrier(0);  // all of those loads issue before the first quantization
+    quant_batch(0);
+    for (int b0 = kXB * nw; b0 < nb; b0 += kXB * nw) {
+      load_batch(b0);
+      quant_batch(b0);
+    }
+    __syncthreads();
+    qa = stage;
+    xa = sd;
+  } else if (LDSQ) {
+    const int nd = nb * 64;
+    for (int i = threadIdx.x * 4; i < nd; i += blockDim.x * 4)
+      *reinterpret_cast<uint4*>(&stage[i]) = *reinterpret_cast<const uint4*>(&qa[i]);
+    __syncthreads();
+    qa = stage;
+    TQ_FETCH(0, 0)
+    TQ_FETCH(1, 1)
+  } else {
+    TQ_FETCH(0, 0)
+    TQ_FETCH(1, 1)
+  }
+  for (int base = 0; base < n; base += RD) {
     TQ_STEP(0) TQ_STEP(1)
   }
 #undef TQ_STEP
@@ -246,13 +298,43 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   const int* qi = reinterpret_cast<const int*>(q);
   const int ns = (int)dm.G8;
 #define TQ_LAUNCH(ID, LQ)                                                                                     \
-  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ>), grid, block, LQ ? (unsigned)stage : 0u, s, codes, \
-                     scales, qi, dx, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
+  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ, false>), grid, block, LQ ? (unsigned)stage : 0u, s, codes, \
+                     scales, qi, dx, nullptr, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
   if (idots) {
     if (ldsq) TQ_LAUNCH(true, true); else TQ_LAUNCH(true, false);
   } else {
     if (ldsq) TQ_LAUNCH(false, true); else TQ_LAUNCH(false, false);
   }
+#undef TQ_LAUNCH
+  return hipGetLastError();
+}
+
+bool gemv_pq2_fused_fits(const Dims& dm, bool have_workspace) {
+  const GemvPlan p = plan_gemv_pq2(dm, have_workspace);
+  return (size_t)p.scw * (256 + 4) <= kMaxStageBytes;
+}
+
+hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* x, float* y, void* workspace,
+                                 hipStream_t s) {
+  constexpr int kRing = 2;
+  const GemvPlan p = plan_gemv_pq2(dm, workspace != nullptr);
+  const size_t stage = (size_t)p.scw * (256 + 4);
+  if (stage > kMaxStageBytes) return hipErrorInvalidValue;  // the caller checks gemv_pq2_fused_fits first
+  const uint4* codes = reinterpret_cast<const uint4*>(w);
+  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
+  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
+  double* partials =
+      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
+  // quantization batch: the blocks one wave quantizes (no more than 8 at once)
+  const int per_wave = (p.scw + p.waves - 1) / p.waves;
+#define TQ_LAUNCH(XB)                                                                                             \
+  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, false, true, true, true, XB>), grid, block, (unsigned)stage, s, codes, \
+                     scales, nullptr, nullptr, reinterpret_cast<const float4*>(x), y, nullptr, (int)dm.rows,        \
+                     (int)dm.nsc, (int)dm.G8, p.scw, p.spw, partials, counters)
+  if (per_wave <= 2) TQ_LAUNCH(2);
+  else if (per_wave <= 4) TQ_LAUNCH(4);
+  else TQ_LAUNCH(8);
 #undef TQ_LAUNCH
   return hipGetLastError();
 }

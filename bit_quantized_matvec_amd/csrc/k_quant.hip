@@ -3,25 +3,16 @@
 // q8_K (ciot README, intro; page 1 "the paperwork"): per block of 256 values,
 // d = max|x| / 127, q = round-to-nearest-even(x / d), and 16 partial sums of
 // 16 consecutive q.  One wave64 owns one block: each lane loads 4 floats (one
-// dwordx4, so the wave reads the block as one coalesced 1 KiB request), the
-// block maximum is a butterfly max-reduction across the wave, and the
-// partial sums are 4-lane butterfly adds.  The divisions are IEEE fp32
-// (correctly rounded; this file must not be built with fast-math), and
-// rintf lowers to v_rndne_f32, so the result is bit-identical to a scalar
-// reference.
+// dwordx4, so the wave reads the block as one coalesced 1 KiB request); the
+// block arithmetic (q8k_block.h) is shared with the matrix-vector kernel that
+// quantizes its own activations; the partial sums are 4-lane butterfly adds.
 #include "kernels.h"
+#include "q8k_block.h"
 
 namespace tq {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-
-__device__ __forceinline__ int quant1(float x, float d) {
-  if (d == 0.0f) return 0;
-  float r = rintf(x / d);
-  r = fminf(127.0f, fmaxf(-127.0f, r));
-  return (int)r;
-}
 
 __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_q8k_kernel(const float4* __restrict__ x, int64_t nblocks,
                                                                            int* __restrict__ q, float* __restrict__ d,
@@ -30,12 +21,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_q8k_kernel(const
   const int64_t blk = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (blk >= nblocks) return;  // whole waves leave together
   const float4 v = x[blk * 64 + lane];
-  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-  const float db = a / 127.0f;
-  const int q0 = quant1(v.x, db), q1 = quant1(v.y, db), q2 = quant1(v.z, db), q3 = quant1(v.w, db);
-  q[blk * 64 + lane] = (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((q3 & 0xff) << 24);
+  const float db = q8k_block_scale(v);
+  const int q0 = q8k_quant1(v.x, db), q1 = q8k_quant1(v.y, db), q2 = q8k_quant1(v.z, db), q3 = q8k_quant1(v.w, db);
+  q[blk * 64 + lane] = q8k_pack4(q0, q1, q2, q3);
   int s = q0 + q1 + q2 + q3;
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);

@@ -39,6 +39,12 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
                                 int32_t* idots, void* workspace, const GemvPlan& p, hipStream_t s);
 hipError_t launch_gemv_pq2(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx, float* y,
                            int32_t* idots, void* workspace, hipStream_t s);
+// The same product from fp32 activations x [cols]: every workgroup quantizes
+// its slice of x to q8_K in LDS (bit-identical to launch_quantize_q8k) and
+// multiplies.  Possible when one slice's q8_K fits the LDS stage.
+bool gemv_pq2_fused_fits(const Dims& dm, bool have_workspace);
+hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* x, float* y, void* workspace,
+                                 hipStream_t s);
 GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace);
 hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
                                  const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,

@@ -114,6 +114,18 @@ int tq_gemv(int fmt, const void* w, int64_t rows, int64_t cols, const int8_t* q,
   return hip_status(tq::launch_gemv_ptq1(wb, dm, q, d, bsums, y, nullptr, workspace, as_stream(stream)));
 }
 
+int tq_gemv_f32(int fmt, const void* w, int64_t rows, int64_t cols, const float* x, float* y, void* workspace,
+                void* stream) {
+  // shape, then what this entry supports (a property of the shape alone), then the pointers
+  const int st = shape_status(fmt, rows, cols, 1);
+  if (st != TQ_OK) return st;
+  const tq::Dims dm = tq::dims(rows, cols);
+  if (fmt != TQ_FMT_PQ2_0 || !tq::gemv_pq2_fused_fits(dm, workspace != nullptr)) return TQ_ERR_UNSUPPORTED;
+  if (!w || !x || !y) return TQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || (workspace && !aligned(workspace, 16))) return TQ_ERR_ALIGN;
+  return hip_status(tq::launch_gemv_pq2_fused(static_cast<const uint8_t*>(w), dm, x, y, workspace, as_stream(stream)));
+}
+
 int tq_gemm(int fmt, const void* w, int64_t rows, int64_t cols, int64_t tokens, const int8_t* q, const float* d,
             const int16_t* bsums, float* y, void* workspace, void* stream) {
   const int st = product_args(fmt, w, rows, cols, tokens, q, d, bsums, y, true);

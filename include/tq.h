@@ -111,9 +111,13 @@ int tq_quantize_q8k(const float *x, int64_t tokens, int64_t cols, int8_t *q, flo
  * 64-row tile (fp64 partial sums plus per-tile arrival counters), which keeps
  * all compute units busy when the row count is small and balances the load
  * when it is large.  Contract: device memory of at least this size, 16-byte
- * aligned, zero-filled once before its first use; every call leaves it zeroed
- * again, so it can be reused by later calls (also inside a captured graph)
- * without clearing.  Calls that run at the same time must not share one.
+ * aligned, zero-filled once before its first use.  It starts with one 32-bit
+ * arrival counter per 64-row tile (rounded up to 256 bytes), which every call
+ * returns to zero; the fp64 partial sums after it are always written before
+ * they are read and keep whatever the last call left.  So it can be reused
+ * by later calls of any shape it is large enough for (also inside a
+ * captured graph) without clearing.  Calls that run at the same time must
+ * not share one.
  * Returns 0 for an invalid shape. */
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens);
 
@@ -128,6 +132,22 @@ int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens);
  * workspace they agree to within the fp64 rounding of the partial sums. */
 int tq_gemv(int fmt, const void *w, int64_t rows, int64_t cols, const int8_t *q, const float *d, const int16_t *bsums,
             float *y, void *workspace, void *stream);
+
+/* Quantize and multiply in one call, one token (page 1, "the paperwork":
+ * activations are squashed to int8 on the fly, right before the product):
+ * x fp32 [cols] -> y fp32 [rows].  Every workgroup quantizes the slice of x
+ * it needs to q8_K in on-chip memory, with the arithmetic of
+ * tq_quantize_q8k, so y is bit-identical to tq_quantize_q8k followed by
+ * tq_gemv (same workspace argument); no q8_K buffer is written.  pq2_0
+ * only.  x: 16-byte aligned, finite.  The q8_K of one
+ * workgroup's column slice must fit on chip (at most 126 blocks of 256, i.e.
+ * 32256 columns): with n = cols / 256 and tiles = ceil(rows / 64), a slice is
+ * ceil(n / s) blocks, s = 1 without a workspace or when tiles >= 384, else
+ * s = min(16, ceil(384 / tiles), max(1, n / 4)).  Shapes beyond that, and
+ * ptq1_0, return TQ_ERR_UNSUPPORTED (checked before the pointers) and touch
+ * nothing. */
+int tq_gemv_f32(int fmt, const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *workspace,
+                void *stream);
 
 /* Matrix product with a small batch of tokens (page 1, "prefill wants a
  * different shape" and "the leftovers"): y[t][r] for t < tokens, the same

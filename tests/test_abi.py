@@ -102,6 +102,37 @@ def test_validation_errors_touch_nothing(tq):
     assert L.tq_last_hip_error() == 0
 
 
+def _fused_fits(rows, cols, ws):
+    """The on-chip rule of tq_gemv_f32 as its declaration states it."""
+    n, tiles = cols // 256, -(-rows // 64)
+    s = 1 if (not ws or tiles >= 384) else min(16, -(-384 // tiles), max(1, n // 4))
+    return -(-n // s) <= 126
+
+
+def test_fused_gemv_validation(tq):
+    L = tq.lib()
+    P = ctypes.c_void_p
+    good, odd = P(0x100000), P(0x100004)
+    assert L.tq_gemv_f32(1, None, 64, 256, good, good, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32(1, good, 64, 256, None, good, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32(1, good, 64, 256, good, None, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32(1, P(0x100008), 64, 256, good, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv_f32(1, good, 64, 256, odd, good, None, None) == tq.ERR_ALIGN  # x needs 16 bytes
+    assert L.tq_gemv_f32(1, good, 64, 256, good, P(0x100002), None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv_f32(1, good, 64, 256, good, good, P(0x100008), None) == tq.ERR_ALIGN
+    assert L.tq_gemv_f32(1, good, 64, 200, good, good, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemv_f32(9, good, 64, 256, good, good, None, None) == tq.ERR_FORMAT
+    assert L.tq_gemv_f32(2, good, 64, 256, None, good, None, None) == tq.ERR_UNSUPPORTED  # ptq1_0
+    # the on-chip limit, both sides of it; it is checked before the pointers,
+    # so the null x below is reached only by shapes that fit
+    for rows, cols, ws in [(64, 32256, None), (64, 32512, None), (24576, 65536, good),
+                           (24512, 65536, good), (64, 65536, good), (64, 262144, good), (64, 1 << 20, good)]:
+        want = tq.ERR_NULL if _fused_fits(rows, cols, ws) else tq.ERR_UNSUPPORTED
+        assert L.tq_gemv_f32(1, good, rows, cols, None, good, ws, None) == want, (rows, cols)
+    assert not _fused_fits(64, 32512, None) and _fused_fits(64, 65536, P(1)) and not _fused_fits(24576, 65536, P(1))
+    assert L.tq_last_hip_error() == 0
+
+
 def test_status_strings(tq):
     L = tq.lib()
     for s in (0, -1, -2, -3, -4, -5, -6, -99):

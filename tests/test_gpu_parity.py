@@ -214,6 +214,85 @@ def test_gemm_grid(tq, orc, R, K):
     say(f"gemm {R}x{K}: {exact}/{total} outputs bit-identical to the oracle")
 
 
+WS_SHAPES = [(1, 256), (5, 1024), (64, 2048), (65, 4096), (200, 8192), (1000, 1280), (3, 16384)]
+
+
+@pytest.mark.parametrize("fmt", ["pq2_0", "ptq1_0"])
+def test_gemv_workspace_split(tq, orc, fmt):
+    """With a workspace, tiles below the split threshold spread their columns
+    over several workgroups; every output still matches the oracle, the
+    arrival counters are back at zero after each call, and a second call
+    gives the same bits, also after a call of another shape in between that
+    shares the workspace."""
+    import torch
+
+    g = TI.rng(77, 12, 1 if fmt == "pq2_0" else 2)
+    ws = tq.workspace(fmt, max(r for r, _ in WS_SHAPES), max(k for _, k in WS_SHAPES))
+    prev = None
+    for R, K in WS_SHAPES:
+        say("gemv workspace", fmt, R, K)
+        W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+        x = TI.activations(g, 1, K)
+        Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
+        q, d, bs = tq.quantize_q8k(dev(x))
+        assert tq.workspace_bytes(fmt, R, K) <= ws.numel()
+        y1 = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
+        assert int(torch.count_nonzero(ws[: 4 * ((R + 63) // 64)])) == 0, "arrival counters not returned to zero"
+        if prev is not None:
+            host(tq.gemv(*prev, ws=ws))
+        y2 = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
+        assert np.array_equal(y1, y2)
+        qo, do, _ = orc.quantize_q8k(x)
+        yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+        assert_close_rows(y1, yo[0], mag[0], what=f"{fmt} {R}x{K} workspace")
+        prev = (fmt, Wd, R, K, q, d, bs)
+
+
+FUSED_CASES = [(1, 256, False), (1, 256, True), (65, 768, False), (200, 2560, True), (64, 8192, False),
+               (33, 8192, True), (500, 1280, True), (7, 32256, False), (130, 65536, True)]
+
+
+@pytest.mark.parametrize("R,K,use_ws", FUSED_CASES)
+def test_gemv_f32_fused(tq, orc, R, K, use_ws):
+    """Quantize-in-the-product entry: bit-identical to quantize_q8k + gemv with
+    the same workspace, and within tolerance of the oracle."""
+    import torch
+
+    g = TI.rng(77, 13, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    x = TI.activations(g, 1, K)
+    x[0, 256:512] = 0.0  # one all-zero block (d = 0) when K allows it
+    say("gemv_f32", R, K, use_ws)
+    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    ws = tq.workspace("pq2_0", R, K) if use_ws else None
+    # x at a 16-byte offset inside a larger buffer
+    xbuf = torch.zeros(K + 8, dtype=torch.float32, device="cuda")
+    xbuf[4:4 + K] = dev(x[0])
+    xd = xbuf[4:4 + K]
+    yf = host(tq.gemv_f32("pq2_0", Wd, R, K, xd, ws=ws))
+    yf2 = host(tq.gemv_f32("pq2_0", Wd, R, K, xd, ws=ws))
+    q, d, bs = tq.quantize_q8k(dev(x))
+    yq = host(tq.gemv("pq2_0", Wd, R, K, q, d, ws=ws))
+    assert np.array_equal(yf, yq) and np.array_equal(yf, yf2)
+    if ws is not None:
+        assert int(torch.count_nonzero(ws[: 4 * ((R + 63) // 64)])) == 0
+    qo, do, _ = orc.quantize_q8k(x)
+    yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
+    assert_close_rows(yf, yo[0], mag[0], what=f"gemv_f32 {R}x{K}")
+
+
+def test_gemv_f32_rejects(tq):
+    import torch
+
+    R, K = 64, 32512
+    Wd = torch.zeros(tq.repacked_bytes("pq2_0", R, K), dtype=torch.uint8, device="cuda")
+    x = torch.zeros(K, dtype=torch.float32, device="cuda")
+    y = torch.full((R,), 7.0, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.gemv_f32("pq2_0", Wd, R, K, x, out=y)
+    assert e.value.status == tq.ERR_UNSUPPORTED and bool(torch.all(y == 7.0))
+
+
 def test_degenerate_inputs(tq, orc):
     g = TI.rng(77, 7)
     R, K = 70, 1024
@@ -272,11 +351,19 @@ def test_tiny_workload_full(tq, orc):
 
 @pytest.mark.parametrize("name", ["decode_32768x8192", "ptq1_32768x8192"])
 def test_decode_workload_full(tq, orc, name):
-    """Every output of the full-size matrix-vector product against the oracle."""
+    """Every output of the full-size matrix-vector product against the oracle,
+    in the launch configuration of the benchmark (with a workspace), and the
+    fused quantize-and-multiply entry bit-identical to it."""
     fmt, W, x = TI.make(name)
     say(name)
     R, G, _ = W.shape
-    _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    ws = tq.workspace(fmt, R, G * 128)
+    qd, dd, bd = tq.quantize_q8k(dev(x))
+    yw = host(tq.gemv(fmt, Wd, R, G * 128, qd, dd, bd, ws=ws))
+    assert np.array_equal(yw, y[0])
+    if fmt == "pq2_0":
+        assert np.array_equal(host(tq.gemv_f32(fmt, Wd, R, G * 128, dev(x[0]), ws=ws)), y[0])
     qo, do, bso = orc.quantize_q8k(x)
     assert np.array_equal(q, qo) and np.array_equal(d, do) and np.array_equal(bs, bso)
     assert np.array_equal(I, orc.group_dots(fmt, W, qo, threads=THREADS))
@@ -310,12 +397,17 @@ def test_step64_shapes_sampled(tq, orc):
         g = TI.rng(TI.STEP64, 0, mi)
         W = TI.pq2_matrix(g, R, K)
         x = TI.activations(g, 1, K)
-        _, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
+        Wd, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
         qo, do, _ = orc.quantize_q8k(x)
         assert np.array_equal(q, qo) and np.array_equal(d, do)
         rows = np.unique(np.concatenate([np.arange(32), np.arange(R - 32, R), TI.rng(77, 10, mi).integers(0, R, 96)]))
         yo, mag = orc.matmul_rows("pq2_0", W, qo, do, rows, with_mag=True)
         assert_close_rows(y[0, rows], yo[0], mag[0], what=name)
+        # the benchmark's launch: a workspace (column split below 384 tiles), and the fused entry
+        ws = tq.workspace("pq2_0", R, K)
+        yw = host(tq.gemv("pq2_0", Wd, R, K, dev(q), dev(d), ws=ws))
+        assert_close_rows(yw[rows], yo[0], mag[0], what=name + " workspace")
+        assert np.array_equal(host(tq.gemv_f32("pq2_0", Wd, R, K, dev(x[0]), ws=ws)), yw)
         assert np.array_equal(I[:, rows, :], orc.group_dots_rows("pq2_0", W, qo, rows))
 
 
