@@ -284,7 +284,8 @@ def ceiling_probe(torch):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_32768x8192.json")
-GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", "k_gemv_pq2.hip")
+# the sources the decode kernel is compiled from: the recorded traffic holds while their hash matches
+GEMV_SOURCES = [os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", f) for f in ("k_gemv_pq2.hip", "q8k_block.h")]
 
 
 def traffic_probe(torch, tq):
@@ -316,16 +317,23 @@ def traffic_probe(torch, tq):
     torch.cuda.synchronize()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the decode kernel from the committed counter
-    runs, or None if the kernel source changed since they were taken."""
+def kernel_source_sha256() -> str:
     import hashlib
 
+    h = hashlib.sha256()
+    for path in GEMV_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter
+    runs, or None if the kernel sources changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(GEMV_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
     return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
