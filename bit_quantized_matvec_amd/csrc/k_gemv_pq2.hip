@@ -13,8 +13,9 @@
 //     each a fully coalesced 1 KiB wave request (the codes are never reused),
 //     plus its row's scale pair, two superchunks ahead of their use;
 //   * the activation bytes a lane needs are the same for every lane of the
-//     wave, so they come in with scalar loads and feed v_dot4_i32_i8 from
-//     SGPRs -- no LDS traffic, no VGPRs;
+//     wave: the workgroup stages its slice of them in LDS once, and each
+//     superchunk's 256 bytes are read from there with broadcast 16-byte
+//     reads, all issued before its products;
 //   * each code dword yields four dot4 operands with one shift and one mask
 //     each ((d << (6-2s)) & 0xC0C0C0C0 = 64*w for four columns: the pages'
 //     slot masking, with two's-complement codes so that no +1 correction is
@@ -37,6 +38,7 @@ constexpr int kMaxWaves = 16;
 constexpr size_t kMaxStageBytes = 32 * 1024;  // LDS for one slice's staged activations
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Weight codes are read once and never reused: non-temporal loads keep them
 // from displacing reusable lines and stream measurably faster on gfx950.
@@ -57,20 +59,24 @@ __device__ __forceinline__ int slot64(uint32_t d, int s) {
 
 // Integer dots of one superchunk: i0 for group 2 sc (dwords c = 0, 1), i1 for
 // group 2 sc + 1 (c = 2, 3).  `a` points at the superchunk's 64 activation
-// dwords (wave-uniform).
+// dwords (wave-uniform); they are fetched first, in one batch of 16-byte
+// reads, so that the wave waits for memory (LDS or cache) once per
+// superchunk rather than once per few products.
 __device__ __forceinline__ void superchunk_dots(const v4u (&v)[4], const int* __restrict__ a, int& i0, int& i1) {
+  v4i act[16];  // act[4c + qd][s] = activation dword 16c + 4qd + s
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    const uint32_t dw[4] = {v[qd][0], v[qd][1], v[qd][2], v[qd][3]};
+  for (int k = 0; k < 16; ++k) act[k] = *reinterpret_cast<const v4i*>(a + 4 * k);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const uint32_t dw = v[qd][c];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int act = a[16 * c + 4 * qd + s];
         if (c < 2)
-          i0 = __builtin_amdgcn_sdot4(slot64(dw[c], s), act, i0, false);
+          i0 = __builtin_amdgcn_sdot4(slot64(dw, s), act[4 * c + qd][s], i0, false);
         else
-          i1 = __builtin_amdgcn_sdot4(slot64(dw[c], s), act, i1, false);
+          i1 = __builtin_amdgcn_sdot4(slot64(dw, s), act[4 * c + qd][s], i1, false);
       }
     }
   }
@@ -80,9 +86,11 @@ __device__ __forceinline__ void superchunk_dots(const v4u (&v)[4], const int* __
 
 // grid = (ntiles, slices).  Workgroup (tile, slice) covers superchunks
 // [slice * scw, min(nsc, (slice + 1) * scw)); its waves take runs of spw.
-// FX: the activations come in as fp32 x (`xf`, `q` and `dx` unused) and each
-// workgroup quantizes its slice to q8_K itself, into LDS (requires LDSQ), in
-// batches of XB blocks per wave (XB at least the blocks per wave, up to 8).
+// LDSQ: the slice's q is copied into LDS first, XB 16-byte pieces per thread
+// (XB at least the pieces per thread).  FX: the activations come in as fp32 x
+// (`xf`, `q` and `dx` unused) and each workgroup quantizes its slice to q8_K
+// itself, into LDS (requires LDSQ), in batches of XB blocks per wave (XB at
+// least the blocks per wave, up to 8).
 template <int RING, bool IDOTS, bool NT, bool LDSQ, bool FX, int XB = 1>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* __restrict__ codes,
                                                                   const uint32_t* __restrict__ scales,
@@ -212,13 +220,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
     qa = stage;
     xa = sd;
   } else if (LDSQ) {
-    const int nd = nb * 64;
-    for (int i = threadIdx.x * 4; i < nd; i += blockDim.x * 4)
-      *reinterpret_cast<uint4*>(&stage[i]) = *reinterpret_cast<const uint4*>(&qa[i]);
-    __syncthreads();
-    qa = stage;
+    // copy of the slice's q: XB 16-byte pieces per thread, all loaded before
+    // the ring's first fetches; a piece index past the slice re-copies its
+    // last piece (same bits to the same place, no branch)
+    const int nd4 = nb * 16;
+    const v4i* src = reinterpret_cast<const v4i*>(qa);
+    v4i* dst = reinterpret_cast<v4i*>(stage);
+    v4i v[XB];
+#pragma unroll
+    for (int i = 0; i < XB; ++i) v[i] = src[min((int)threadIdx.x + i * (int)blockDim.x, nd4 - 1)];
     TQ_FETCH(0, 0)
     TQ_FETCH(1, 1)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < XB; ++i) dst[min((int)threadIdx.x + i * (int)blockDim.x, nd4 - 1)] = v[i];
+    __syncthreads();
+    qa = stage;
   } else {
     TQ_FETCH(0, 0)
     TQ_FETCH(1, 1)
@@ -297,14 +314,23 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   const bool ldsq = stage <= kMaxStageBytes;
   const int* qi = reinterpret_cast<const int*>(q);
   const int ns = (int)dm.G8;
-#define TQ_LAUNCH(ID, LQ)                                                                                     \
-  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ, false>), grid, block, LQ ? (unsigned)stage : 0u, s, codes, \
-                     scales, qi, dx, nullptr, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
+  // 16-byte pieces of q per thread in the LDS copy
+  const int pieces = (p.scw * 16 + 64 * p.waves - 1) / (64 * p.waves);
+#define TQ_LAUNCH(ID, LQ, XB)                                                                                     \
+  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ, false, XB>), grid, block, LQ ? (unsigned)stage : 0u, s, \
+                     codes, scales, qi, dx, nullptr, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
+#define TQ_LAUNCH_Q(ID)                          \
+  if (!ldsq) TQ_LAUNCH(ID, false, 1);            \
+  else if (pieces <= 1) TQ_LAUNCH(ID, true, 1);  \
+  else if (pieces <= 2) TQ_LAUNCH(ID, true, 2);  \
+  else if (pieces <= 4) TQ_LAUNCH(ID, true, 4);  \
+  else TQ_LAUNCH(ID, true, 8);
   if (idots) {
-    if (ldsq) TQ_LAUNCH(true, true); else TQ_LAUNCH(true, false);
+    TQ_LAUNCH_Q(true)
   } else {
-    if (ldsq) TQ_LAUNCH(false, true); else TQ_LAUNCH(false, false);
+    TQ_LAUNCH_Q(false)
   }
+#undef TQ_LAUNCH_Q
 #undef TQ_LAUNCH
   return hipGetLastError();
 }
