@@ -15,15 +15,17 @@
 //     dwords whose fields are columns 64c + 16qd + [0, 16), c = 0..3 -- the A
 //     operands of four v_mfma_i32_16x16x64_i8 after one shift and one mask
 //     per field) and one 16-byte load of its four rows' scale pairs.
-//   * The activations of the superchunk (16 * NT tokens x 256 bytes) and the
-//     tokens' d_x are shared by the four waves through a double-buffered LDS
-//     stage: fetched row by row (coalesced), stored at [token][piece ^
-//     (token & 15)] so that neither the stores nor the operand reads (16
-//     tokens, one piece) collide in LDS banks; one barrier per superchunk.
-//   * Every stream is fetched D superchunks ahead into register rings with
-//     literal indices.  The loop's first pass only fetches, so the state at
-//     the loop header is the steady state and the compiler's wait counts stay
-//     exact (no drain per pass).
+//   * The activations of the superchunk (16 * NT tokens x 256 bytes) are
+//     shared by the four waves through a double-buffered LDS stage: fetched
+//     row by row (coalesced), stored at [token][piece ^ (token & 15)] so that
+//     neither the stores nor the operand reads (16 tokens, one piece) collide
+//     in LDS banks; one barrier per superchunk.  The tokens' d_x for every
+//     superchunk are copied into LDS once, before the loop.
+//   * Codes, scales and activations are fetched D superchunks ahead into
+//     register rings with literal indices.  A prologue fills the ring and the
+//     main loop runs only while every fetch is real, so its body has no
+//     branch and the compiler's wait counts stay exact (no drain per pass);
+//     the last passes run in a separate tail loop.
 //   * Epilogue per superchunk, in fp64 (every product exact, sums rounded
 //     once per operation): inner = d_w(2sc+1) * I1 + d_w(2sc) * I0, then
 //     y += (d_x / 64) * inner; the 1/64 removes the scale of the
@@ -43,6 +45,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kDepth = 4;
+
+// LDS of the d_x copy: 16 * NT tokens x nsc superchunks of fp32, at most
+// 32 KiB (rows of up to 65536 columns with 32-token blocks)
+constexpr size_t gemm_dx_bytes(int nsc, int nt) { return (size_t)nsc * 16 * nt * 4; }
+constexpr size_t kMaxDxBytes = 32 * 1024;
 
 __device__ __forceinline__ v4i expand64(uint32_t d) {
   v4i a;
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
   constexpr int BPT = BPIECES / 256;  // per thread
   constexpr int D = kDepth;
   __shared__ v4u lds_b[2][BPIECES];
-  __shared__ float lds_x[2][NTOK];
+  extern __shared__ float lds_x[];  // d_x of the block's tokens, [superchunk][token]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int rb = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,13 +103,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     b_src[k] = q + (size_t)min(tok0 + t, tokens - 1) * K + 16 * p;  // + sc * 256
     b_dst[k] = t * 16 + (p ^ (t & 15));
   }
-  // d_x of token tid % NTOK (the group-dot variant has no d_x: it reads a
-  // scale word instead, which is never used)
-  const int xt = min(tok0 + (tid % NTOK), tokens - 1);
-  const float* x_src = IDOTS ? reinterpret_cast<const float*>(scales) : dx + (size_t)xt * nsc;  // + sc
-
   v4u ra[D], rs[D], rbv[D][BPT];
-  float rx[D];
   // Fetches past the last superchunk read cache-resident activation bytes in
   // place of codes and scales (no HBM traffic); every load stays
   // unconditional so that the wait counts stay exact.
@@ -115,7 +116,6 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     rs[J] = *(real ? s_src + (size_t)scf * 16 : dummy);                                  \
     _Pragma("unroll") for (int k = 0; k < BPT; ++k) rbv[J][k] =                          \
         *reinterpret_cast<const v4u*>(b_src[k] + (size_t)scf * 256);                     \
-    rx[J] = x_src[scf];                                                                  \
   }
 
   double yacc[NT][4];
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     } else {
       double xd[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) xd[n] = (double)lds_x[buf][16 * n + l16] * 0.015625;
+      for (int n = 0; n < NT; ++n) xd[n] = (double)lds_x[sc * NTOK + 16 * n + l16] * 0.015625;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const double d0 = lo_half(s4[v]), d1 = hi_half(s4[v]);
@@ -170,25 +170,49 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     }
   };
 
-  // Step J of a pass: publish superchunk j's activations and d_x in LDS
-  // buffer j & 1, multiply, then fetch superchunk j + D into the freed ring
-  // slot.  The barrier also guarantees that every wave is done with buffer
-  // j & 1 from two steps back before it is overwritten.
-#define TQ_STEP(J)                                                                      \
+  // d_x of every superchunk for the block's tokens, copied into LDS once (the
+  // group-dot variant has no d_x).  The first 4 * 256 values are loaded into
+  // registers ahead of the ring's first fetches (an index past the end
+  // re-copies the last value: same bits, same place, no branch); the rest, for
+  // long rows only, after them.
+  constexpr int XPT = 4;
+  const int nx = nsc * NTOK;
+  float xr[XPT];
+  auto x_at = [&](int i) { return dx[(size_t)min(tok0 + i % NTOK, tokens - 1) * nsc + i / NTOK]; };
+  if (!IDOTS) {
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) xr[k] = x_at(min(tid + 256 * k, nx - 1));
+  }
+
+  // Step J of a pass: publish superchunk j's activations in LDS buffer j & 1,
+  // multiply, then fetch superchunk j + D into the freed ring slot.  The
+  // barrier also guarantees that every wave is done with buffer j & 1 from
+  // two steps back before it is overwritten (and, at the first step, that
+  // the d_x copy is complete).
+#define TQ_STEP(J, LIVE)                                                                \
   {                                                                                     \
     const int j = base + J;                                                             \
-    if (j >= 0 && j < nsc) {                                                            \
+    if (LIVE) {                                                                         \
       const int buf = j & 1;                                                            \
       _Pragma("unroll") for (int k = 0; k < BPT; ++k) lds_b[buf][b_dst[k]] = rbv[J][k]; \
-      if (tid < NTOK) lds_x[buf][tid] = rx[J];                                          \
       __syncthreads();                                                                  \
       compute(buf, ra[J], rs[J], j);                                                    \
     }                                                                                   \
     TQ_FETCH(J, j + D)                                                                  \
   }
 
-  for (int base = -D; base < nsc; base += D) {
-    TQ_STEP(0) TQ_STEP(1) TQ_STEP(2) TQ_STEP(3)
+  TQ_FETCH(0, 0) TQ_FETCH(1, 1) TQ_FETCH(2, 2) TQ_FETCH(3, 3)
+  if (!IDOTS) {
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) lds_x[min(tid + 256 * k, nx - 1)] = xr[k];
+    for (int i = tid + 256 * XPT; i < nx; i += 256) lds_x[i] = x_at(i);
+  }
+  int base = 0;
+  for (; base + 2 * D <= nsc; base += D) {
+    TQ_STEP(0, true) TQ_STEP(1, true) TQ_STEP(2, true) TQ_STEP(3, true)
+  }
+  for (; base < nsc; base += D) {
+    TQ_STEP(0, j < nsc) TQ_STEP(1, j < nsc) TQ_STEP(2, j < nsc) TQ_STEP(3, j < nsc)
   }
 #undef TQ_STEP
 #undef TQ_FETCH
@@ -219,8 +243,8 @@ hipError_t launch_gemm_nt(const uint8_t* w, const Dims& dm, int64_t tokens, cons
     hipLaunchKernelGGL((gemm_pq2_kernel<NT, true>), grid, block, 0, s, codes, scales, q, dx, y, idots, (int)dm.rows,
                        (int)dm.ntiles, nsc, (int)tokens, ntb);
   else
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, false>), grid, block, 0, s, codes, scales, q, dx, y, idots, (int)dm.rows,
-                       (int)dm.ntiles, nsc, (int)tokens, ntb);
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, false>), grid, block, (unsigned)gemm_dx_bytes(nsc, NT), s, codes, scales, q,
+                       dx, y, idots, (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb);
   return hipGetLastError();
 }
 
@@ -232,7 +256,17 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
   // 17408 x 5120 prompt shape: the 16-token kernel has more independent
   // workgroups per CU, the 32-token one shares each code expansion and scale
   // conversion between twice the tokens)
-  if (tokens <= 32) return launch_gemm_nt<1>(w, dm, tokens, q, dx, y, idots, s);
+  const int nt = tokens <= 32 ? 1 : 2;
+  if (gemm_dx_bytes((int)dm.nsc, nt) > kMaxDxBytes) {
+    // rows longer than the d_x copy allows: one matrix-vector product per token
+    for (int64_t t = 0; t < tokens; ++t) {
+      const hipError_t e = launch_gemv_pq2(w, dm, q + t * dm.cols, dx + t * dm.nsc, y + t * dm.rows,
+                                           idots ? idots + t * dm.rows * 2 * dm.nsc : nullptr, nullptr, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (nt == 1) return launch_gemm_nt<1>(w, dm, tokens, q, dx, y, idots, s);
   return launch_gemm_nt<2>(w, dm, tokens, q, dx, y, idots, s);
 }
 

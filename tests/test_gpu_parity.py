@@ -411,6 +411,22 @@ def test_step64_shapes_sampled(tq, orc):
         assert np.array_equal(I[:, rows, :], orc.group_dots_rows("pq2_0", W, qo, rows))
 
 
+@pytest.mark.parametrize("R,K,T", [(65, 65536, 40), (3, 65792, 40), (5, 131072, 5), (2, 131328, 3)])
+def test_gemm_long_rows(tq, orc, R, K, T):
+    """Prompt products on rows past the limit of the d_x copy fall back to one
+    matrix-vector product per token; both sides of that limit agree with the
+    oracle."""
+    g = TI.rng(77, 14, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    x = TI.activations(g, T, K)
+    say("gemm long rows", R, K, T)
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
+    qo, do, _ = orc.quantize_q8k(x)
+    assert np.array_equal(I, orc.group_dots("pq2_0", W, qo))
+    yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
+    assert_close_rows(y, yo, mag, what=f"gemm {R}x{K} T={T}")
+
+
 def test_max_columns(tq, orc):
     g = TI.rng(77, 11)
     for fmt, K in (("pq2_0", 65536), ("ptq1_0", 32768)):
