@@ -27,8 +27,10 @@
 namespace tq {
 namespace {
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 8;   // the kernel's limit
+constexpr int kPlanWaves = 4;  // what the plan uses
 constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock
+constexpr int kQChunk = 4;                      // superblocks of q copied into LDS at a time
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h));
@@ -38,11 +40,12 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 // q[col(group gi, byte 4m + i, trit j)] with D = 6 gi + m.  Entry (48 + p, j, h):
 // the leftover dword p pairs bytes 24, 25 of groups 2p (h = 0) and 2p + 1
 // (h = 1); only the half of the dword that belongs to group 2p + h is non-zero.
-__device__ uint32_t table_entry(const int8_t* __restrict__ q, int G, int sb, int e) {
+// `qs` is the workgroup's copy of q in LDS, starting at group g0.
+__device__ uint32_t table_entry(const uint8_t* __restrict__ qs, int g0, int G, int sb, int e) {
   auto act = [&](int g, int byte, int j) -> uint32_t {
     const int k = 5 * byte + j;  // position inside the group
     if (g >= G || k >= 128) return 0u;
-    return (uint32_t)(uint8_t)q[(size_t)g * 128 + k];
+    return (uint32_t)qs[(g - g0) * 128 + k];
   };
   if (e < 48 * 8) {
     const int D = e >> 3, j = e & 7;
@@ -85,10 +88,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
   const int wg0 = slice * scw;
   const int wg1 = min(G8, wg0 + scw);
 
-  // permuted activations of this workgroup's superblocks
-  for (int e = threadIdx.x; e < (wg1 - wg0) * kTableDwords; e += blockDim.x)
-    table[e] = table_entry(q, G, wg0 + e / kTableDwords, e % kTableDwords);
-  __syncthreads();
+  // Permuted activations of this workgroup's superblocks, built kQChunk
+  // superblocks at a time: that part of q is first copied into LDS with
+  // coalesced 16-byte loads (the table gathers single bytes, which straight
+  // from global memory would cost one round trip each), then its table
+  // entries are built from the copy.
+  uint8_t* qs = reinterpret_cast<uint8_t*>(table + (wg1 - wg0) * kTableDwords);
+  for (int c0 = wg0; c0 < wg1; c0 += kQChunk) {
+    const int c1 = min(wg1, c0 + kQChunk);
+    const int g0 = c0 * 8, g1 = min(G, c1 * 8);
+    const uint4* src = reinterpret_cast<const uint4*>(q + (size_t)g0 * 128);
+    uint4* dst = reinterpret_cast<uint4*>(qs);
+    for (int i = threadIdx.x; i < (g1 - g0) * 8; i += blockDim.x) dst[i] = src[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < (c1 - c0) * kTableDwords; e += blockDim.x) {
+      const int sb = c0 + e / kTableDwords;
+      table[(sb - wg0) * kTableDwords + e % kTableDwords] = table_entry(qs, g0, G, sb, e % kTableDwords);
+    }
+    __syncthreads();
+  }
 
   const int sb0 = min(wg1, wg0 + wave * spw);
   const int sb1 = min(wg1, sb0 + spw);
@@ -213,7 +231,9 @@ GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
   }
   p.scw = (G8 + slices - 1) / slices;
   p.slices = (G8 + p.scw - 1) / p.scw;
-  const int waves = p.scw < kMaxWaves ? p.scw : kMaxWaves;
+  // up to 4 waves (measured on 32768 x 8192: 4 waves of two superblocks each
+  // beat 8 waves of one, which cannot share a CU two workgroups at a time)
+  const int waves = p.scw < kPlanWaves ? p.scw : kPlanWaves;
   p.spw = (p.scw + waves - 1) / waves;
   p.waves = (p.scw + p.spw - 1) / p.spw;
   return p;
@@ -222,7 +242,8 @@ GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
 hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
                                  const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,
                                  hipStream_t s) {
-  const size_t lds = (size_t)p.scw * kTableDwords * sizeof(uint32_t);
+  // the table, then room for kQChunk superblocks of q to build it from
+  const size_t lds = (size_t)p.scw * kTableDwords * sizeof(uint32_t) + (size_t)kQChunk * 1024;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
   unsigned* counters = reinterpret_cast<unsigned*>(workspace);

@@ -14,7 +14,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int64_t kMaxCols = int64_t(1) << 20;
 constexpr int64_t kMaxWeights = int64_t(1) << 36;
 constexpr int64_t kMaxTokens = int64_t(1) << 20;
-constexpr int64_t kMaxPtq1Cols = 32768;  // the ptq1_0 activation table (1792 B per 1024 cols) stays under 64 KiB of LDS
+constexpr int64_t kMaxPtq1Cols = 32768;  // the ptq1_0 activation table (1792 B per 1024 cols) and a 4 KiB copy of q stay within 64 KiB of LDS
 
 bool fmt_ok(int f) { return f == TQ_FMT_PQ2_0 || f == TQ_FMT_PTQ1_0; }
 
