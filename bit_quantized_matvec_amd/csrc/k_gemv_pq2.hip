@@ -202,8 +202,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
       for (int i = 0; i < kXB; ++i) {
         const int b = min(b0 + wave + i * nw, nb - 1);
         const float db = q8k_block_scale(v[i]);
-        stage[b * 64 + lane] =
-            q8k_pack4(q8k_quant1(v[i].x, db), q8k_quant1(v[i].y, db), q8k_quant1(v[i].z, db), q8k_quant1(v[i].w, db));
+        stage[b * 64 + lane] = q8k_quant4(v[i], db);
         if (lane == 0) sd[b] = db;
       }
     };

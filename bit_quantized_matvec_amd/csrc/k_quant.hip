@@ -22,9 +22,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void quantize_q8k_kernel(const
   if (blk >= nblocks) return;  // whole waves leave together
   const float4 v = x[blk * 64 + lane];
   const float db = q8k_block_scale(v);
-  const int q0 = q8k_quant1(v.x, db), q1 = q8k_quant1(v.y, db), q2 = q8k_quant1(v.z, db), q3 = q8k_quant1(v.w, db);
-  q[blk * 64 + lane] = q8k_pack4(q0, q1, q2, q3);
-  int s = q0 + q1 + q2 + q3;
+  const int packed = q8k_quant4(v, db);
+  q[blk * 64 + lane] = packed;
+  int s = (int)(int8_t)packed + (int)(int8_t)(packed >> 8) + (int)(int8_t)(packed >> 16) + (int)(int8_t)(packed >> 24);
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
   if ((lane & 3) == 0) bsums[blk * 16 + (lane >> 2)] = (int16_t)s;

@@ -6,8 +6,10 @@
 // q8_K (ciot README, intro; page 1 "the paperwork"): d = max|x| / 127 and
 // q = round-to-nearest-even(x / d), both in IEEE fp32.  The divisions are
 // correctly rounded (no fast-math in this library) and rintf lowers to
-// v_rndne_f32, so the result is bit-identical to a scalar reference.  The
-// maximum is exact in any order, so its reduction order is free.
+// v_rndne_f32, so the result is bit-identical to a scalar reference; the
+// per-value divisions are replaced by one reciprocal per block wherever that
+// provably gives the same integer (q8k_quant4).  The maximum is exact in any
+// order, so its reduction order is free.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -48,6 +50,38 @@ __device__ __forceinline__ int q8k_quant1(float x, float d) {
 // The lane's four quantized values packed little-endian into a dword.
 __device__ __forceinline__ int q8k_pack4(int q0, int q1, int q2, int q3) {
   return (q0 & 0xff) | ((q1 & 0xff) << 8) | ((q2 & 0xff) << 16) | ((q3 & 0xff) << 24);
+}
+
+// The lane's four values quantized and packed, bit-identical to q8k_quant1
+// on each, with one division per block instead of one per value.
+//
+// With r = fl(1/d), the product y = fl(x * r) is within 3 * 2^-24 * |x/d| of
+// the correctly rounded quotient fl(x/d) (two roundings of relative size
+// 2^-24 each, plus the quotient's own), i.e. within 2^-15 since |x/d| <= 127
+// (up to rounding) in a q8_K block.  If y lies farther than 2^-15 from every
+// half-integer, fl(x/d) and y round to the same integer; otherwise (and for
+// non-finite y, or a block scale below 2^-100 where 1/d may overflow) the
+// value takes the exact path.  A wave takes the exact path only when one of
+// its lanes needs it.
+__device__ __forceinline__ int q8k_quant4(const float4 v, float d) {
+  if (d == 0.0f) return 0;
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  int qv[4];
+  if (d >= 0x1p-100f) {
+    const float r = 1.0f / d;
+    bool exact = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = x[i] * r;
+      const float k = rintf(y);
+      // |y - k| is the distance to the nearest integer; a half-integer is near
+      // when it exceeds 0.5 - 2^-15 (NaN compares false: exact path)
+      exact |= !(fabsf(y - k) < 0.5f - 0x1p-15f);
+      qv[i] = (int)k;
+    }
+    if (!exact) return q8k_pack4(qv[0], qv[1], qv[2], qv[3]);
+  }
+  return q8k_pack4(q8k_quant1(x[0], d), q8k_quant1(x[1], d), q8k_quant1(x[2], d), q8k_quant1(x[3], d));
 }
 
 }  // namespace tq

@@ -93,6 +93,19 @@ def quant_cases():
         x[0, i] = float(xv)
     yield "ties", x
     yield "odd_tokens", TI.activations(g, 7, 256)
+    # values within a few ulps of half-integer multiples of the block scale
+    # (the quantizer's reciprocal fast path must hand these to the exact path)
+    x = np.zeros((6, 256), np.float32)
+    for t in range(6):
+        amax = np.float32(g.uniform(0.5, 300.0))
+        d = np.float32(amax / np.float32(127.0))
+        k = g.integers(-126, 126, size=255).astype(np.float32)
+        near = ((k + np.float32(0.5)) * d).astype(np.float32)
+        steps = g.integers(-3, 4, size=255)
+        x[t, 0] = amax
+        x[t, 1:] = np.nextafter(near, np.where(steps > 0, np.inf, -np.inf).astype(np.float32)).astype(np.float32)
+        x[t, 1:] = np.where(steps == 0, near, x[t, 1:])
+    yield "near_half_integers", x
 
 
 @pytest.mark.parametrize("case", [c for c, _ in quant_cases()])
