@@ -37,6 +37,7 @@ _SIGS = {
     "tq_workspace_bytes": ([_i32, _i64, _i64, _i64], _i64),
     "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_gemv_f32": ([_i32, _p, _i64, _i64, _p, _p, _p, _p], _i32),
+    "tq_gemv_f32_batch": ([_i32, _i32, _p, _p, _i64, _p, _p, _p, _p], _i32),
     "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_group_dots": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_status_str": ([_i32], ctypes.c_char_p),
@@ -172,6 +173,26 @@ def gemv_f32(fmt, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, out=No
         out = torch.empty(rows, dtype=torch.float32, device=w.device)
     _check(_lib.tq_gemv_f32(_fmt(fmt), _ptr(w), rows, cols, _ptr(x), _ptr(out), _ptr(ws), _stream()), "tq_gemv_f32")
     return out
+
+
+def gemv_f32_batch(fmt, ws_list, rows, cols: int, xs, outs=None, ws=None):
+    """Independent gemv_f32 products sharing `cols`, in one launch: problem m
+    multiplies ws_list[m] (rows[m] x cols) by xs[m]; returns the outputs."""
+    n = len(ws_list)
+    if not (len(rows) == len(xs) == n):
+        raise TQError(ERR_SHAPE, "gemv_f32_batch: list lengths differ")
+    for x in xs:
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.numel() != cols:
+            raise TQError(ERR_SHAPE, "gemv_f32_batch: every x must be a contiguous float32 tensor of cols elements")
+    if outs is None:
+        outs = [torch.empty(r, dtype=torch.float32, device=w.device) for w, r in zip(ws_list, rows)]
+    P = ctypes.c_void_p * max(n, 1)
+    wp = P(*[t.data_ptr() for t in ws_list])
+    xp = P(*[t.data_ptr() for t in xs])
+    yp = P(*[t.data_ptr() for t in outs])
+    rp = (ctypes.c_int64 * max(n, 1))(*rows)
+    _check(_lib.tq_gemv_f32_batch(_fmt(fmt), n, wp, rp, cols, xp, yp, _ptr(ws), _stream()), "tq_gemv_f32_batch")
+    return outs
 
 
 def gemm(fmt, w: torch.Tensor, rows: int, cols: int, q, d, bsums=None, out=None, ws=None) -> torch.Tensor:

@@ -43,6 +43,21 @@ hipError_t launch_gemv_pq2(const uint8_t* w, const Dims& dm, const int8_t* q, co
 // its slice of x to q8_K in LDS (bit-identical to launch_quantize_q8k) and
 // multiplies.  Possible when one slice's q8_K fits the LDS stage.
 bool gemv_pq2_fused_fits(const Dims& dm, bool have_workspace);
+
+// Independent fused products sharing one column count, launched together:
+// problem m covers workgroups [tile0[m], tile0[m + 1]).
+constexpr int kMaxBatch = 4;
+struct GemvBatch {
+  const uint4* codes[kMaxBatch];
+  const uint32_t* scales[kMaxBatch];
+  const float4* x[kMaxBatch];
+  float* y[kMaxBatch];
+  int rows[kMaxBatch];
+  int tile0[kMaxBatch + 1];
+  int n;
+};
+// `dm` describes the whole batch: ntiles = tile0[n], cols the common count
+hipError_t launch_gemv_pq2_fused_batch(const GemvBatch& b, const Dims& dm, void* workspace, hipStream_t s);
 hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* x, float* y, void* workspace,
                                  hipStream_t s);
 GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace);

@@ -126,6 +126,40 @@ int tq_gemv_f32(int fmt, const void* w, int64_t rows, int64_t cols, const float*
   return hip_status(tq::launch_gemv_pq2_fused(static_cast<const uint8_t*>(w), dm, x, y, workspace, as_stream(stream)));
 }
 
+int tq_gemv_f32_batch(int fmt, int n, const void* const* w, const int64_t* rows, int64_t cols, const float* const* x,
+                      float* const* y, void* workspace, void* stream) {
+  if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;
+  if (n < 1 || n > tq::kMaxBatch) return TQ_ERR_SHAPE;
+  if (!w || !rows || !x || !y) return TQ_ERR_NULL;
+  int64_t tiles = 0;
+  for (int m = 0; m < n; ++m) {
+    const int st = shape_status(fmt, rows[m], cols, 1);
+    if (st != TQ_OK) return st;
+    tiles += (rows[m] + 63) / 64;
+  }
+  if (shape_status(fmt, tiles * 64, cols, 1) != TQ_OK) return TQ_ERR_SHAPE;
+  const tq::Dims dm = tq::dims(tiles * 64, cols);
+  if (fmt != TQ_FMT_PQ2_0 || !tq::gemv_pq2_fused_fits(dm, workspace != nullptr)) return TQ_ERR_UNSUPPORTED;
+  tq::GemvBatch b{};
+  b.n = n;
+  b.tile0[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    if (!w[m] || !x[m] || !y[m]) return TQ_ERR_NULL;
+    if (!aligned(w[m], 16) || !aligned(x[m], 16) || !aligned(y[m], 4)) return TQ_ERR_ALIGN;
+    const tq::Dims dmm = tq::dims(rows[m], cols);
+    const uint8_t* wb = static_cast<const uint8_t*>(w[m]);
+    b.codes[m] = reinterpret_cast<const uint4*>(wb);
+    b.scales[m] = reinterpret_cast<const uint32_t*>(wb + tq::pq2_code_bytes(dmm));
+    b.x[m] = reinterpret_cast<const float4*>(x[m]);
+    b.y[m] = y[m];
+    b.rows[m] = (int)rows[m];
+    b.tile0[m + 1] = b.tile0[m] + (int)dmm.ntiles;
+  }
+  for (int m = n; m < tq::kMaxBatch; ++m) b.tile0[m + 1] = b.tile0[n];
+  if (workspace && !aligned(workspace, 16)) return TQ_ERR_ALIGN;
+  return hip_status(tq::launch_gemv_pq2_fused_batch(b, dm, workspace, as_stream(stream)));
+}
+
 int tq_gemm(int fmt, const void* w, int64_t rows, int64_t cols, int64_t tokens, const int8_t* q, const float* d,
             const int16_t* bsums, float* y, void* workspace, void* stream) {
   const int st = product_args(fmt, w, rows, cols, tokens, q, d, bsums, y, true);

@@ -149,6 +149,24 @@ int tq_gemv(int fmt, const void *w, int64_t rows, int64_t cols, const int8_t *q,
 int tq_gemv_f32(int fmt, const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *workspace,
                 void *stream);
 
+/* Several independent tq_gemv_f32 products with the same column count in one
+ * launch (page 1, "what's running": a decode step runs one product after
+ * another for every projection of every layer; products that do not depend
+ * on one another, such as the gate and up projections of a layer, can share
+ * a launch).  Problem m (m < n, 1 <= n <= 4): w[m] (repacked pq2_0, rows[m] x
+ * cols), x[m] fp32 [cols] (16-byte aligned), y[m] fp32 [rows[m]].  The
+ * host arrays w, rows, x and y are read during the call only.  Each y[m] is
+ * the same as a tq_gemv_f32 call would give it with the same workspace
+ * treatment for a matrix of all the problems' row tiles together: with no
+ * workspace, or 384 or more row tiles in total, bit-identical to separate
+ * tq_gemv_f32 calls without a workspace.  `workspace` (nullable): at least
+ * tq_workspace_bytes(fmt, R, cols, 1) bytes, R = the sum of the rows[m] each
+ * rounded up to a multiple of 64.  The on-chip rule of tq_gemv_f32 applies
+ * to that R (TQ_ERR_UNSUPPORTED, checked before the per-problem pointers).
+ * pq2_0 only. */
+int tq_gemv_f32_batch(int fmt, int n, const void *const *w, const int64_t *rows, int64_t cols, const float *const *x,
+                      float *const *y, void *workspace, void *stream);
+
 /* Matrix product with a small batch of tokens (page 1, "prefill wants a
  * different shape" and "the leftovers"): y[t][r] for t < tokens, the same
  * arithmetic as tq_gemv per token.  Token counts that are not a multiple of

@@ -133,6 +133,30 @@ def test_fused_gemv_validation(tq):
     assert L.tq_last_hip_error() == 0
 
 
+def test_fused_batch_validation(tq):
+    L = tq.lib()
+    P = ctypes.c_void_p
+    good, odd = P(0x100000), P(0x100004)
+    A = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    R = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    w2, x2, y2, r2 = A(good, good), A(good, good), A(good, good), R(64, 128)
+    assert L.tq_gemv_f32_batch(1, 0, w2, r2, 256, x2, y2, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemv_f32_batch(1, 5, w2, r2, 256, x2, y2, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemv_f32_batch(9, 2, w2, r2, 256, x2, y2, None, None) == tq.ERR_FORMAT
+    assert L.tq_gemv_f32_batch(1, 2, None, r2, 256, x2, y2, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32_batch(1, 2, w2, None, 256, x2, y2, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32_batch(1, 2, w2, R(64, 0), 256, x2, y2, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemv_f32_batch(1, 2, w2, r2, 200, x2, y2, None, None) == tq.ERR_SHAPE
+    assert L.tq_gemv_f32_batch(2, 2, w2, r2, 256, x2, y2, None, None) == tq.ERR_UNSUPPORTED  # ptq1_0
+    # the on-chip rule on the total row tiles, before the per-problem pointers
+    assert L.tq_gemv_f32_batch(1, 2, A(None, None), R(64, 64), 32512, x2, y2, None, None) == tq.ERR_UNSUPPORTED
+    assert L.tq_gemv_f32_batch(1, 2, A(good, None), R(64, 64), 256, x2, y2, None, None) == tq.ERR_NULL
+    assert L.tq_gemv_f32_batch(1, 2, w2, r2, 256, A(good, odd), y2, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv_f32_batch(1, 2, A(good, P(0x100008)), r2, 256, x2, y2, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv_f32_batch(1, 2, w2, r2, 256, x2, y2, P(0x100008), None) == tq.ERR_ALIGN
+    assert L.tq_last_hip_error() == 0
+
+
 def test_status_strings(tq):
     L = tq.lib()
     for s in (0, -1, -2, -3, -4, -5, -6, -99):

@@ -294,6 +294,34 @@ def test_gemv_f32_fused(tq, orc, R, K, use_ws):
     assert_close_rows(yf, yo[0], mag[0], what=f"gemv_f32 {R}x{K}")
 
 
+@pytest.mark.parametrize("rows,K", [([200, 333], 2560), ([64, 1, 130, 65], 1024), ([7000], 768), ([6000, 6000], 512)])
+def test_gemv_f32_batch(tq, orc, rows, K):
+    """Independent fused products in one launch: without a workspace each
+    output is bit-identical to its own tq_gemv_f32 call; with one (column
+    splits when the total is below 384 tiles) within tolerance of the oracle,
+    and the arrival counters are back at zero."""
+    import torch
+
+    g = TI.rng(77, 15, len(rows), K)
+    Ws = [TI.pq2_matrix(g, R, K) for R in rows]
+    xs = [TI.activations(g, 1, K) for _ in rows]
+    say("gemv_f32_batch", rows, K)
+    Wd = [tq.repack(dev(W.reshape(-1)), "pq2_0", R, K) for W, R in zip(Ws, rows)]
+    xd = [dev(x[0]) for x in xs]
+    ys = [host(y) for y in tq.gemv_f32_batch("pq2_0", Wd, rows, K, xd)]
+    for m, R in enumerate(rows):
+        assert np.array_equal(ys[m], host(tq.gemv_f32("pq2_0", Wd[m], R, K, xd[m]))), m
+    R64 = sum(-(-R // 64) * 64 for R in rows)
+    ws = tq.workspace("pq2_0", R64, K)
+    yw = [host(y) for y in tq.gemv_f32_batch("pq2_0", Wd, rows, K, xd, ws=ws)]
+    assert int(torch.count_nonzero(ws[: 4 * (R64 // 64)])) == 0
+    for m, R in enumerate(rows):
+        qo, do, _ = orc.quantize_q8k(xs[m])
+        yo, mag = orc.matmul("pq2_0", Ws[m], qo, do, with_mag=True)
+        assert_close_rows(ys[m], yo[0], mag[0], what=f"batch {m} {R}x{K}")
+        assert_close_rows(yw[m], yo[0], mag[0], what=f"batch {m} {R}x{K} workspace")
+
+
 def test_gemv_f32_rejects(tq):
     import torch
 
