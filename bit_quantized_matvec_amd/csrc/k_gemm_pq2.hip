@@ -73,7 +73,7 @@ template <int NT, bool IDOTS>
 __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ codes, const uint32_t* __restrict__ scales,
                                                        const int8_t* __restrict__ q, const float* __restrict__ dx,
                                                        float* __restrict__ y, int32_t* __restrict__ idots, int rows,
-                                                       int ntiles, int nsc, int tokens, int ntb) {
+                                                       int ntiles, int nsc, int tokens, int ntb, int spw) {
   constexpr int NTOK = 16 * NT;
   constexpr int BPIECES = NTOK * 16;  // 16-byte activation pieces per superchunk
   constexpr int BPT = BPIECES / 256;  // per thread
@@ -118,11 +118,26 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
         *reinterpret_cast<const v4u*>(b_src[k] + (size_t)scf * 256);                     \
   }
 
-  double yacc[NT][4];
+  // yacc sums the superchunks of one run of spw, ytot the finished runs in
+  // order: the summation order of the matrix-vector product (one run per
+  // wave, waves added in order), so each token's output is bit-identical to
+  // a tq_gemv call without a workspace
+  double yacc[NT][4], ytot[NT][4];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) yacc[n][v] = 0.0;
+    for (int v = 0; v < 4; ++v) yacc[n][v] = ytot[n][v] = 0.0;
+  auto fold_run = [&](int j) __attribute__((always_inline)) {
+    if (j + 1 == nsc || (j + 1) % spw == 0) {  // uniform
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          ytot[n][v] = j < spw ? yacc[n][v] : ytot[n][v] + yacc[n][v];
+          yacc[n][v] = 0.0;
+        }
+    }
+  };
 
   auto compute = [&](int buf, const v4u c4, const v4u s4, int sc) __attribute__((always_inline)) {
     v4i acc[2][NT];
@@ -197,6 +212,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
       _Pragma("unroll") for (int k = 0; k < BPT; ++k) lds_b[buf][b_dst[k]] = rbv[J][k]; \
       __syncthreads();                                                                  \
       compute(buf, ra[J], rs[J], j);                                                    \
+      if (!IDOTS) fold_run(j);                                                          \
     }                                                                                   \
     TQ_FETCH(J, j + D)                                                                  \
   }
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int t = tok0 + 16 * n + l16;
-      if (row < rows && t < tokens) y[(size_t)t * rows + row] = (float)yacc[n][v];
+      if (row < rows && t < tokens) y[(size_t)t * rows + row] = (float)ytot[n][v];
     }
   }
 }
@@ -239,12 +255,14 @@ hipError_t launch_gemm_nt(const uint8_t* w, const Dims& dm, int64_t tokens, cons
   const dim3 grid((unsigned)(groups * 8 * ntb)), block(256);
   const v4u* codes = reinterpret_cast<const v4u*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
+  // the run length of the matrix-vector product without a workspace
+  const int spw = plan_gemv_pq2(dm, false).spw;
   if (idots)
     hipLaunchKernelGGL((gemm_pq2_kernel<NT, true>), grid, block, 0, s, codes, scales, q, dx, y, idots, (int)dm.rows,
-                       (int)dm.ntiles, nsc, (int)tokens, ntb);
+                       (int)dm.ntiles, nsc, (int)tokens, ntb, spw);
   else
     hipLaunchKernelGGL((gemm_pq2_kernel<NT, false>), grid, block, (unsigned)gemm_dx_bytes(nsc, NT), s, codes, scales, q,
-                       dx, y, idots, (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb);
+                       dx, y, idots, (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb, spw);
   return hipGetLastError();
 }
 

@@ -137,10 +137,14 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
         idots[(size_t)row * G + 2 * sc + 1] = I1;
       }
     } else {
-      // s2: fp16 scales of groups 2sc (low half) and 2sc+1
+      // s2: fp16 scales of groups 2sc (low half) and 2sc+1.  The pair's
+      // inner sum d0 I0 + d1 I1 (the first product exact) is rounded once,
+      // then scaled by d_x into the accumulator: the prompt product's
+      // epilogue, so that both give the same bits
       const double dxs = (double)xa[sc - wg0];
-      acc += ((double)half_bits_to_float(s2 & 0xffffu) * dxs) * (double)I0;
-      acc += ((double)half_bits_to_float(s2 >> 16) * dxs) * (double)I1;
+      const double inner = __builtin_fma((double)half_bits_to_float(s2 >> 16), (double)I1,
+                                         (double)half_bits_to_float(s2 & 0xffffu) * (double)I0);
+      acc = __builtin_fma(dxs, inner, acc);
     }
   };
 

@@ -171,7 +171,11 @@ int tq_gemv_f32_batch(int fmt, int n, const void *const *w, const int64_t *rows,
  * different shape" and "the leftovers"): y[t][r] for t < tokens, the same
  * arithmetic as tq_gemv per token.  Token counts that are not a multiple of
  * the kernel's tile are padded internally; padded outputs are never written.
- * A single token runs the matrix-vector kernel.  `workspace` as for tq_gemv. */
+ * A single token runs the matrix-vector kernel.  `workspace` as for tq_gemv;
+ * with more than one token it is not used.  For pq2_0 and tokens > 1, y[t] is
+ * bit-identical to tq_gemv of token t without a workspace (the same rounding
+ * of each group pair's sum and the same summation order), so a batch of a few
+ * tokens gives exactly the outputs of one product per token. */
 int tq_gemm(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q, const float *d,
             const int16_t *bsums, float *y, void *workspace, void *stream);
 

@@ -227,6 +227,32 @@ def test_gemm_grid(tq, orc, R, K):
     say(f"gemm {R}x{K}: {exact}/{total} outputs bit-identical to the oracle")
 
 
+@pytest.mark.parametrize("R,K", [(64, 256), (130, 1280), (200, 2048), (65, 3328), (17408, 5120)])
+def test_gemm_equals_stacked_gemv(tq, R, K):
+    """A prompt product of T tokens gives, bit for bit, the outputs of T
+    matrix-vector products without a workspace: both round each group pair's
+    inner sum once and sum the superchunks in the same runs and run order.
+    The column counts give runs of 1, 2, 2, 4 and 5 superchunks with ragged
+    last runs; 17408x5120 is the prefill shape."""
+    import torch
+
+    g = TI.rng(77, 15, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    for T in (2, 3, 4, 5, 6, 7, 8, 17, 64):
+        say("gemm vs gemv", R, K, T)
+        x = TI.activations(g, T, K)
+        q, d, bs = tq.quantize_q8k(dev(x))
+        y = host(tq.gemm("pq2_0", Wd, R, K, q, d, bs))
+        yv = np.stack([host(tq.gemv("pq2_0", Wd, R, K, q[t], d[t])) for t in range(T)])
+        assert np.array_equal(y, yv), (R, K, T, int(np.sum(y != yv)))
+        if T <= 8:
+            yf = np.stack([host(tq.gemv_f32("pq2_0", Wd, R, K, dev(x[t]))) for t in range(T)])
+            assert np.array_equal(y, yf), (R, K, T, "fused")
+    del Wd
+    torch.cuda.empty_cache()
+
+
 WS_SHAPES = [(1, 256), (5, 1024), (64, 2048), (65, 4096), (200, 8192), (1000, 1280), (3, 16384)]
 
 
