@@ -144,8 +144,9 @@ def decode_bench(torch, tq, K, W):
     }
 
 
-def prefill_bench(torch, tq, T, K):
-    fmt, Wc, x = TI.make("prefill_17408x5120_t64" if T == 64 else "prefill_17408x5120_t4")
+def prefill_bench(torch, tq, T, K, fmt_name="pq2_0"):
+    prefix = "prefill" if fmt_name == "pq2_0" else "ptq1_prefill"
+    fmt, Wc, x = TI.make(f"{prefix}_17408x5120_t{T}")
     R, G, _ = Wc.shape
     C = G * 128
     wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
@@ -161,8 +162,12 @@ def prefill_bench(torch, tq, T, K):
     torch.cuda.synchronize()
     us = batch_us(torch, call, K)
     macs = R * C * T
-    return {"tokens": T, "us": us, "gmac_s": macs / us / 1e3, "mfma_frac": 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12),
-            "hbm_gbs": (tq.repacked_bytes(fmt, R, C) + T * C + 4 * T * (C // 256) + 4 * T * R) / us / 1e3}
+    r = {"tokens": T, "us": us, "gmac_s": macs / us / 1e3}
+    if fmt == "pq2_0":  # int8 matrix cores; ptq1_0 takes its dot products on the vector units
+        r["mfma_frac"] = 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12)
+    bsum_bytes = 2 * T * (C // 16) if fmt == "ptq1_0" else 0
+    r["hbm_gbs"] = (tq.repacked_bytes(fmt, R, C) + T * C + bsum_bytes + 4 * T * (C // 256) + 4 * T * R) / us / 1e3
+    return r
 
 
 def ptq1_bench(torch, tq, K):
@@ -437,6 +442,9 @@ def main():
         extra["step64"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in step64_bench(torch, tq, 5).items()}
         p = ptq1_bench(torch, tq, 200)
         extra["ptq1_decode"] = {k: round(v, 4) for k, v in p.items()}
+        for T in (4, 64):
+            p = prefill_bench(torch, tq, T, 100, "ptq1_0")
+            extra[f"ptq1_prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
         extra["quantize_8192"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in quantize_bench(torch, tq, 200).items()}
         extra["ceiling"] = {k: round(v, 1) for k, v in ceiling_probe(torch).items()}
     out["extra"] = extra

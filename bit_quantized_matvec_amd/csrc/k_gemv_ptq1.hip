@@ -19,106 +19,166 @@
 //     over 128 values is one add over 8 partial sums);
 //   * the dot4 partner of trit j of four consecutive code bytes is the four
 //     activations 5 apart; each workgroup first writes this permuted copy of
-//     q into LDS, and the main loop reads it with wave-uniform (broadcast)
-//     LDS loads.  The two bytes per group that do not fill a dword are paired
-//     with the next group's, and their padding trits meet zero activations.
+//     q into LDS (20 consecutive bytes of q give the 5 entries of one code
+//     dword: a 4 x 5 byte transpose), and the main loop reads it with
+//     wave-uniform (broadcast) LDS loads.  The two bytes per group that do
+//     not fill a dword are paired with the next group's, and their padding
+//     trits meet zero activations;
+//   * the fp64 sum has one fixed order whatever the launch: the terms of a
+//     superblock's 8 groups are added in group order from zero, and the
+//     superblock sums in superblock order.  Waves, column slices (with a
+//     workspace) and token blocks only change who computes which superblock
+//     sum, so every launch shape gives the same bits;
+//   * a prompt of several tokens runs NT tokens per workgroup (NT = 1, 2, 4
+//     or 8): each code dword is decoded once and its trits meet the NT
+//     tokens' tables, whose entries are interleaved by token.
 #include "kernels.h"
 
 namespace tq {
 namespace {
 
 constexpr int kMaxWaves = 8;   // the kernel's limit
-constexpr int kPlanWaves = 4;  // what the plan uses
-constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock
-constexpr int kQChunk = 4;                      // superblocks of q copied into LDS at a time
+constexpr int kPlanWaves = 4;  // what the one-token plan uses
+constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock and token
+constexpr int kTasks = 48 + 8;                  // table-building tasks per superblock and token
+constexpr int kMaxTokBlock = 8;                 // tokens per workgroup
+constexpr size_t kLdsBudget = 80 * 1024;        // two workgroups per compute unit
+
+// Dynamic LDS of a workgroup: the tables of scw superblocks for nt tokens.
+// Once a superblock's products are done, the start of its table holds its
+// fp64 sums [token][lane] (512 bytes per token, within the 1792 of the table).
+size_t ptq1_lds_bytes(int scw, int nt) { return (size_t)nt * scw * kTableDwords * sizeof(uint32_t); }
+
+// `L` consecutive dwords of LDS from a 16-byte aligned address, in as few
+// reads as the alignment allows.
+template <int L>
+__device__ __forceinline__ void lds_run(const uint32_t* p, uint32_t* v) {
+  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < L / 4; ++i) {
+    const uint4 t = p4[i];
+    v[4 * i] = t.x;
+    v[4 * i + 1] = t.y;
+    v[4 * i + 2] = t.z;
+    v[4 * i + 3] = t.w;
+  }
+  if constexpr (L % 4 >= 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p + L / 4 * 4);
+    v[L / 4 * 4] = t.x;
+    v[L / 4 * 4 + 1] = t.y;
+  }
+  if constexpr (L % 2 == 1) v[L - 1] = p[L - 1];
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h));
 }
 
-// Permuted activation table.  Entry (D < 48, j): bytes i = 0..3 hold
-// q[col(group gi, byte 4m + i, trit j)] with D = 6 gi + m.  Entry (48 + p, j, h):
-// the leftover dword p pairs bytes 24, 25 of groups 2p (h = 0) and 2p + 1
-// (h = 1); only the half of the dword that belongs to group 2p + h is non-zero.
-// `qs` is the workgroup's copy of q in LDS, starting at group g0.
-__device__ uint32_t table_entry(const uint8_t* __restrict__ qs, int g0, int G, int sb, int e) {
-  auto act = [&](int g, int byte, int j) -> uint32_t {
-    const int k = 5 * byte + j;  // position inside the group
-    if (g >= G || k >= 128) return 0u;
-    return (uint32_t)qs[(g - g0) * 128 + k];
-  };
-  if (e < 48 * 8) {
-    const int D = e >> 3, j = e & 7;
-    if (j >= 5) return 0u;
-    const int g = sb * 8 + D / 6, m = D % 6;
-    uint32_t r = 0;
-    for (int i = 0; i < 4; ++i) r |= act(g, 4 * m + i, j) << (8 * i);
-    return r;
+// Permuted activation table of one superblock and token.  Entry (D, j),
+// D = 6 gi + m < 48, j < 5, at dword 8 D + j: bytes i = 0..3 hold
+// q[group 8 sb + gi][5 (4m + i) + j], the partners of trit j of code bytes
+// 4m .. 4m + 3 of that group.  Entry (p, h, j) at dword 384 + 16 p + 2 j + h:
+// the leftover code dword p pairs bytes 24, 25 of groups 2p (low half) and
+// 2p + 1 (high half); entry h holds group 2p + h's partners of trit j of
+// those two bytes in its half and zeros in the other.  Groups past G and
+// positions past 128 (the padding trits of byte 25) are zero.
+//
+// Task t < 48 (D = t) reads the 20 bytes q[g][20m .. 20m + 19] and writes
+// the five entries (D, 0..4), a 4 x 5 byte transpose; task 48 + 2p + h reads
+// q[g][120 .. 127] and writes the five entries (p, h, 0..4).  `qt` is the
+// token's row of q; `out` the superblock's table, `nt` tokens interleaved.
+__device__ __forceinline__ void build_task(const int8_t* __restrict__ qt, int G, int sb, int task, uint32_t* out,
+                                           int nt) {
+  auto byte = [](uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; };
+  if (task < 48) {
+    const int g = sb * 8 + task / 6, m = task % 6;
+    uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+    if (g < G) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(qt + (size_t)g * 128 + 20 * m);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) w[k] = src[k];
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      uint32_t r = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 5 * i + j;  // byte of the 20
+        r |= byte(w[b >> 2], b & 3) << (8 * i);
+      }
+      out[(task * 8 + j) * nt] = r;
+    }
+  } else {
+    const int p = (task - 48) >> 1, h = (task - 48) & 1;
+    const int g = sb * 8 + 2 * p + h;
+    uint32_t u0 = 0u, u1 = 0u;  // q[g][120 .. 123], q[g][124 .. 127]
+    if (g < G) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(qt + (size_t)g * 128 + 120);
+      u0 = src[0];
+      u1 = src[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const uint32_t a = j < 4 ? byte(u0, j) : byte(u1, 0);  // q[120 + j]
+      const uint32_t b = j < 3 ? byte(u1, j + 1) : 0u;       // q[125 + j]; 128, 129 are padding
+      const uint32_t lo = a | (b << 8);
+      out[(384 + 16 * p + 2 * j + h) * nt] = h ? lo << 16 : lo;
+    }
   }
-  const int f = e - 48 * 8;
-  const int p = f >> 4, jj = f & 15;
-  if (jj >= 10) return 0u;
-  const int j = jj >> 1, h = jj & 1;
-  const int g = sb * 8 + 2 * p + h;
-  const uint32_t lo = act(g, 24, j) | (act(g, 25, j) << 8);
-  return h ? lo << 16 : lo;
 }
 
 }  // namespace
 
-// grid = (ntiles, slices).  Workgroup (tile, slice) covers superblocks
-// [slice * scw, min(G8, (slice + 1) * scw)); its waves take runs of spw.
-template <bool IDOTS>
+// grid = (ntiles, slices, token blocks).  Workgroup (tile, slice, tb) covers
+// superblocks [slice * scw, min(G8, (slice + 1) * scw)) for tokens
+// [tb * NT, tb * NT + NT) (those past `tokens` are padding: zero tables,
+// outputs not written); its waves take runs of spw superblocks.  Several
+// slices are used with NT == 1 only.
+template <bool IDOTS, int NT>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* __restrict__ codes,
                                                                    const uint4* __restrict__ scales,
                                                                    const int8_t* __restrict__ q, const float* __restrict__ dx,
                                                                    const int16_t* __restrict__ bsums, float* __restrict__ y,
                                                                    int32_t* __restrict__ idots, int rows, int G, int G8,
                                                                    int scw, int spw, double* __restrict__ partials,
-                                                                   unsigned* __restrict__ counters) {
-  extern __shared__ uint32_t table[];
-  __shared__ double red[kMaxWaves][64];
+                                                                   unsigned* __restrict__ counters, int tokens) {
+  extern __shared__ __align__(16) uint32_t table[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int tile = blockIdx.x;
   const int slice = blockIdx.y;
   const int nslices = gridDim.y;
+  const int tok0 = blockIdx.z * NT;
   const int row = tile * 64 + lane;
   const int wg0 = slice * scw;
   const int wg1 = min(G8, wg0 + scw);
+  const size_t K = (size_t)G * 128;
 
-  // Permuted activations of this workgroup's superblocks, built kQChunk
-  // superblocks at a time: that part of q is first copied into LDS with
-  // coalesced 16-byte loads (the table gathers single bytes, which straight
-  // from global memory would cost one round trip each), then its table
-  // entries are built from the copy.
-  uint8_t* qs = reinterpret_cast<uint8_t*>(table + (wg1 - wg0) * kTableDwords);
-  for (int c0 = wg0; c0 < wg1; c0 += kQChunk) {
-    const int c1 = min(wg1, c0 + kQChunk);
-    const int g0 = c0 * 8, g1 = min(G, c1 * 8);
-    const uint4* src = reinterpret_cast<const uint4*>(q + (size_t)g0 * 128);
-    uint4* dst = reinterpret_cast<uint4*>(qs);
-    for (int i = threadIdx.x; i < (g1 - g0) * 8; i += blockDim.x) dst[i] = src[i];
-    __syncthreads();
-    for (int e = threadIdx.x; e < (c1 - c0) * kTableDwords; e += blockDim.x) {
-      const int sb = c0 + e / kTableDwords;
-      table[(sb - wg0) * kTableDwords + e % kTableDwords] = table_entry(qs, g0, G, sb, e % kTableDwords);
-    }
-    __syncthreads();
+  // Permuted activations of this workgroup's superblocks: entry e of
+  // superblock sb for token n sits at ((sb - wg0) * kTableDwords + e) * NT + n.
+  for (int i = threadIdx.x; i < (wg1 - wg0) * kTasks * NT; i += blockDim.x) {
+    const int n = i % NT, r = i / NT;
+    const int sb = wg0 + r / kTasks, task = r % kTasks;
+    uint32_t* out = table + (size_t)(sb - wg0) * kTableDwords * NT + n;
+    if (tok0 + n < tokens) build_task(q + (size_t)(tok0 + n) * K, G, sb, task, out, NT);
+    else build_task(q, 0, sb, task, out, NT);  // padding token: G = 0 gives zero entries
   }
+  __syncthreads();
 
   const int sb0 = min(wg1, wg0 + wave * spw);
   const int sb1 = min(wg1, sb0 + spw);
-  double acc = 0.0;
   for (int sb = sb0; sb < sb1; ++sb) {
+    double acc[NT];  // this superblock's sums, from zero
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = 0.0;
     // Loads 0..11 hold the 48 full dwords (3 loads per group pair), load 12
     // the four leftover dwords.  One group pair is decoded per iteration,
     // with the next pair's three loads already in flight.
     const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
     const uint4 left = cp[12 * 64];
     const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
-    const uint32_t* tb = table + (sb - wg0) * kTableDwords;
+    const uint32_t* tb = table + (size_t)(sb - wg0) * kTableDwords * NT;
     uint4 cur[3] = {cp[0], cp[64], cp[128]};
 #pragma unroll 1
     for (int gp = 0; gp < 4; ++gp) {
@@ -131,21 +191,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       const uint32_t dws[13] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z,
                                 cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
                                 gp == 0 ? left.x : gp == 1 ? left.y : gp == 2 ? left.z : left.w};
-      int ia = 0, ib = 0;  // groups 2 gp and 2 gp + 1
+      int ia[NT], ib[NT];  // groups 2 gp and 2 gp + 1, per token
+#pragma unroll
+      for (int n = 0; n < NT; ++n) ia[n] = ib[n] = 0;
+      // Table entries of dword m: 5 levels (10 level-halves for the leftover
+      // dword m = 12) x NT tokens, entry (level, token) at te[level * NT + token].
+      // With one token all reads of a dword are issued together and the
+      // compiler schedules them; with more, the reads of dword m + 1 are
+      // issued before the products of dword m and no earlier (opaque offsets
+      // and accumulators order them), so that two dwords' entries at most
+      // are held in registers.
+      constexpr int kLev = 5 * NT, kLeft = 10 * NT;
+      constexpr bool kAll = NT == 1;
+      auto te_off = [&](int m) { return m < 12 ? (12 * gp + m) * 8 * NT : (48 * 8 + gp * 16) * NT; };
+      uint32_t tnext[kLeft];
+      if constexpr (!kAll) {
+        int off = te_off(0);
+        asm volatile("" : "+v"(off));
+        lds_run<kLev>(tb + off, tnext);
+      }
 #pragma unroll
       for (int m = 0; m < 13; ++m) {
         const uint32_t d = dws[m];
-        uint32_t tv[10];
-        if (m < 12) {
-          const uint32_t* te = tb + (12 * gp + m) * 8;
-          const uint4 t0 = *reinterpret_cast<const uint4*>(te);
-          tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w; tv[4] = te[4];
+        uint32_t tv[kLeft];
+        if constexpr (kAll) {
+          const uint32_t* te = tb + te_off(m);
+          if (m < 12) lds_run<kLev>(te, tv);
+          else lds_run<kLeft>(te, tv);
         } else {
-          const uint4* lt = reinterpret_cast<const uint4*>(tb + 48 * 8 + gp * 16);
-          const uint4 t0 = lt[0], t1 = lt[1];
-          const uint2 t2 = *reinterpret_cast<const uint2*>(lt + 2);
-          tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w;
-          tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w; tv[8] = t2.x; tv[9] = t2.y;
+#pragma unroll
+          for (int i = 0; i < kLeft; ++i) tv[i] = tnext[i];
+          if (m + 1 < 13) {
+            int off = te_off(m + 1);
+            asm volatile("" : "+v"(off));
+            if (m + 1 < 12) lds_run<kLev>(tb + off, tnext);
+            else lds_run<kLeft>(tb + off, tnext);
+          }
         }
         uint32_t e = d & 0x00FF00FFu;
         uint32_t o = (d >> 8) & 0x00FF00FFu;
@@ -156,16 +237,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
           // each 16-bit lane now holds 3v < 768, so its high byte is the trit:
           // one byte permute gathers the four (bytes 1, 3 of e and of o)
           const int t = (int)__builtin_amdgcn_perm(o, e, 0x07030501u);
-          if (m < 6) {
-            ia = __builtin_amdgcn_sdot4(t, (int)tv[j], ia, false);
-          } else if (m < 12) {
-            ib = __builtin_amdgcn_sdot4(t, (int)tv[j], ib, false);
-          } else {
-            ia = __builtin_amdgcn_sdot4(t, (int)tv[2 * j], ia, false);
-            ib = __builtin_amdgcn_sdot4(t, (int)tv[2 * j + 1], ib, false);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            if (m < 6) {
+              ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ia[n], false);
+            } else if (m < 12) {
+              ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ib[n], false);
+            } else {
+              ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[2 * j * NT + n], ia[n], false);
+              ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[(2 * j + 1) * NT + n], ib[n], false);
+            }
           }
           e &= 0x00FF00FFu;
           o &= 0x00FF00FFu;
+        }
+        if constexpr (!kAll) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
         }
       }
       const uint32_t s2 = gp == 0 ? sc8.x : gp == 1 ? sc8.y : gp == 2 ? sc8.z : sc8.w;
@@ -173,13 +261,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       for (int h = 0; h < 2; ++h) {
         const int g = sb * 8 + 2 * gp + h;
         if (g < G) {
-          const int16_t* bs = bsums + (size_t)g * 8;
-          const int qsum = bs[0] + bs[1] + bs[2] + bs[3] + bs[4] + bs[5] + bs[6] + bs[7];
-          const int I = (h ? ib : ia) - qsum;
-          if (IDOTS) {
-            if (row < rows) idots[(size_t)row * G + g] = I;
-          } else {
-            acc += ((double)half_bits_to_float(h ? (s2 >> 16) : (s2 & 0xffffu)) * (double)dx[g >> 1]) * (double)I;
+          const double dw = (double)half_bits_to_float(h ? (s2 >> 16) : (s2 & 0xffffu));
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const int t = min(tok0 + n, tokens - 1);
+            const int16_t* bs = bsums + t * K / 16 + (size_t)g * 8;
+            const int qsum = bs[0] + bs[1] + bs[2] + bs[3] + bs[4] + bs[5] + bs[6] + bs[7];
+            const int I = (h ? ib[n] : ia[n]) - qsum;
+            if (IDOTS) {
+              if (row < rows && tok0 + n < tokens) idots[((size_t)t * rows + row) * G + g] = I;
+            } else {
+              acc[n] += (dw * (double)dx[t * K / 256 + (g >> 1)]) * (double)I;
+            }
           }
         }
       }
@@ -187,23 +280,37 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       cur[1] = nxt[1];
       cur[2] = nxt[2];
     }
+    if (!IDOTS) {
+      // this wave has read the last of the superblock's table (LDS operations
+      // of one wave complete in order): its sums take the table's place
+      double* red = reinterpret_cast<double*>(table + (size_t)(sb - wg0) * kTableDwords * NT);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) red[n * 64 + lane] = acc[n];
+    }
   }
   if (IDOTS) return;
-  red[wave][lane] = acc;
   __syncthreads();
-  if (wave != 0) return;
-  double s = red[0][lane];
-  for (int w = 1; w < nw; ++w) s += red[w][lane];
+  auto sb_sum = [&](int sb, int n) {
+    return reinterpret_cast<const double*>(table + (size_t)(sb - wg0) * kTableDwords * NT)[n * 64 + lane];
+  };
   if (nslices == 1) {
-    if (row < rows) y[row] = (float)s;
+    // token n is summed by wave n mod nw, superblock by superblock
+    for (int n = wave; n < NT; n += nw) {
+      double s = sb_sum(wg0, n);
+      for (int sb = wg0 + 1; sb < wg1; ++sb) s += sb_sum(sb, n);
+      if (row < rows && tok0 + n < tokens) y[(size_t)(tok0 + n) * rows + row] = (float)s;
+    }
     return;
   }
-  // several slices per tile: the last workgroup to arrive sums them in order
-  // The partial goes out with an agent-scope atomic store (written through
-  // to the level shared by all XCDs, so no whole-L2 write-back is needed);
-  // the counter is bumped only after the store has completed (vmcnt = 0).
-  __hip_atomic_store(&partials[((size_t)tile * nslices + slice) * 64 + lane], s, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  if (wave != 0) return;
+  // Several slices per tile (one token): the superblock sums go to the
+  // workspace with agent-scope atomic stores (written through to the level
+  // shared by all XCDs, so no whole-L2 write-back is needed); the counter is
+  // bumped only after the stores have completed (vmcnt = 0).  The last
+  // workgroup to arrive adds all the tile's superblock sums in order.
+  for (int sb = wg0; sb < wg1; ++sb)
+    __hip_atomic_store(&partials[((size_t)tile * G8 + sb) * 64 + lane], sb_sum(sb, 0), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   unsigned prev = 0;
@@ -211,9 +318,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
   prev = __shfl(prev, 0, 64);
   if (prev != (unsigned)(nslices - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  double t = 0.0;
-  for (int k = 0; k < nslices; ++k)
-    t += __hip_atomic_load(&partials[((size_t)tile * nslices + k) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  double t = __hip_atomic_load(&partials[(size_t)tile * G8 * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int sb = 1; sb < G8; ++sb)
+    t += __hip_atomic_load(&partials[((size_t)tile * G8 + sb) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (row < rows) y[row] = (float)t;
   if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -239,23 +346,41 @@ GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
   return p;
 }
 
+namespace {
+
+template <bool IDOTS, int NT>
+void launch_ptq1(const dim3& grid, const dim3& block, size_t lds, hipStream_t s, const uint4* codes,
+                 const uint4* scales, const int8_t* q, const float* dx, const int16_t* bsums, float* y, int32_t* idots,
+                 const Dims& dm, const GemvPlan& p, double* partials, unsigned* counters, int tokens) {
+  hipLaunchKernelGGL((gemv_ptq1_kernel<IDOTS, NT>), grid, block, lds, s, codes, scales, q, dx, bsums, y, idots,
+                     (int)dm.rows, (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters, tokens);
+}
+
+template <int NT>
+void launch_ptq1_nt(bool idots_out, const dim3& grid, const dim3& block, size_t lds, hipStream_t s,
+                    const uint4* codes, const uint4* scales, const int8_t* q, const float* dx, const int16_t* bsums,
+                    float* y, int32_t* idots, const Dims& dm, const GemvPlan& p, double* partials, unsigned* counters,
+                    int tokens) {
+  if (idots_out)
+    launch_ptq1<true, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, partials, counters, tokens);
+  else
+    launch_ptq1<false, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, partials, counters,
+                           tokens);
+}
+
+}  // namespace
+
 hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
                                  const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,
                                  hipStream_t s) {
-  // the table, then room for kQChunk superblocks of q to build it from
-  const size_t lds = (size_t)p.scw * kTableDwords * sizeof(uint32_t) + (size_t)kQChunk * 1024;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
   unsigned* counters = reinterpret_cast<unsigned*>(workspace);
   double* partials =
       workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
-  if (idots)
-    hipLaunchKernelGGL(gemv_ptq1_kernel<true>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
-                       (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters);
-  else
-    hipLaunchKernelGGL(gemv_ptq1_kernel<false>, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, (int)dm.rows,
-                       (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters);
+  launch_ptq1_nt<1>(idots != nullptr, grid, block, ptq1_lds_bytes(p.scw, 1), s, codes, scales, q, dx, bsums, y, idots,
+                    dm, p, partials, counters, 1);
   return hipGetLastError();
 }
 
@@ -263,6 +388,39 @@ hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, c
                             float* y, int32_t* idots, void* workspace, hipStream_t s) {
   const GemvPlan p = plan_gemv_ptq1(dm, workspace != nullptr && idots == nullptr);
   return launch_gemv_ptq1_plan(w, dm, q, dx, bsums, y, idots, workspace, p, s);
+}
+
+int ptq1_token_block(const Dims& dm, int64_t tokens) {
+  // the smallest power of two covering the tokens, at most 8, and no more
+  // than the LDS budget holds
+  const GemvPlan p = plan_gemv_ptq1(dm, false);
+  int nt = 1;
+  while (nt < kMaxTokBlock && nt < tokens && ptq1_lds_bytes(p.scw, 2 * nt) <= kLdsBudget) nt *= 2;
+  return nt;
+}
+
+hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
+                            const int16_t* bsums, float* y, int32_t* idots, hipStream_t s) {
+  // one workgroup per tile and token block, up to 8 waves of one or more
+  // superblocks each (the summation order does not depend on the split)
+  GemvPlan p = plan_gemv_ptq1(dm, false);
+  const int waves = p.scw < kMaxWaves ? p.scw : kMaxWaves;
+  p.spw = (p.scw + waves - 1) / waves;
+  p.waves = (p.scw + p.spw - 1) / p.spw;
+  const int nt = ptq1_token_block(dm, tokens);
+  const uint4* codes = reinterpret_cast<const uint4*>(w);
+  const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
+  const dim3 grid((unsigned)dm.ntiles, 1u, (unsigned)((tokens + nt - 1) / nt)), block(64 * p.waves);
+  const size_t lds = ptq1_lds_bytes(p.scw, nt);
+  const bool io = idots != nullptr;
+  const int T = (int)tokens;
+  switch (nt) {
+    case 1: launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
+    case 2: launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
+    case 4: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
+    default: launch_ptq1_nt<8>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace tq

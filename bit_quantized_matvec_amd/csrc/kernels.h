@@ -20,9 +20,13 @@ constexpr int kMaxSlices = 16;
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Workspace of the split products: per-tile arrival counters (zero between
-// calls), then fp64 partial sums [tile][slice][64].
+// calls), then fp64 partial sums, [tile][slice][64] for pq2_0 and
+// [tile][superblock][64] for ptq1_0.
 inline int64_t workspace_counter_bytes(const Dims& d) { return (d.ntiles * 4 + 255) / 256 * 256; }
-inline int64_t workspace_bytes(const Dims& d) { return workspace_counter_bytes(d) + d.ntiles * kMaxSlices * 64 * 8; }
+inline int64_t workspace_bytes(const Dims& d, bool ptq1) {
+  const int64_t per_tile = ptq1 && d.G8 > kMaxSlices ? d.G8 : kMaxSlices;
+  return workspace_counter_bytes(d) + d.ntiles * per_tile * 64 * 8;
+}
 
 hipError_t launch_quantize_q8k(const float* x, int64_t nblocks, int8_t* q, float* d, int16_t* bsums, hipStream_t s);
 
@@ -66,6 +70,11 @@ hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t*
                                  hipStream_t s);
 hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, const float* dx,
                             const int16_t* bsums, float* y, int32_t* idots, void* workspace, hipStream_t s);
+// Several tokens: y[tokens][rows] or idots [tokens][rows][G], each token
+// bit-identical to launch_gemv_ptq1 without a workspace.
+int ptq1_token_block(const Dims& dm, int64_t tokens);
+hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
+                            const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
 // y[tokens][rows] or idots [tokens][rows][G].
 hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                            float* y, int32_t* idots, hipStream_t s);

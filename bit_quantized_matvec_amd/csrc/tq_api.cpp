@@ -100,7 +100,7 @@ int tq_quantize_q8k(const float* x, int64_t tokens, int64_t cols, int8_t* q, flo
 
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens) {
   if (shape_status(fmt, rows, cols, tokens) != TQ_OK) return 0;
-  return tq::workspace_bytes(tq::dims(rows, cols));
+  return tq::workspace_bytes(tq::dims(rows, cols), fmt == TQ_FMT_PTQ1_0);
 }
 
 int tq_gemv(int fmt, const void* w, int64_t rows, int64_t cols, const int8_t* q, const float* d, const int16_t* bsums,
@@ -167,10 +167,11 @@ int tq_gemm(int fmt, const void* w, int64_t rows, int64_t cols, int64_t tokens, 
   if (workspace && !aligned(workspace, 16)) return TQ_ERR_ALIGN;
   // A single token takes the matrix-vector kernel (page 1, "the leftovers").
   if (tokens == 1) return tq_gemv(fmt, w, rows, cols, q, d, bsums, y, workspace, stream);
-  if (fmt != TQ_FMT_PQ2_0) return TQ_ERR_UNSUPPORTED;
   const tq::Dims dm = tq::dims(rows, cols);
-  return hip_status(
-      tq::launch_gemm_pq2(static_cast<const uint8_t*>(w), dm, tokens, q, d, y, nullptr, as_stream(stream)));
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  if (fmt == TQ_FMT_PTQ1_0)
+    return hip_status(tq::launch_gemm_ptq1(wb, dm, tokens, q, d, bsums, y, nullptr, as_stream(stream)));
+  return hip_status(tq::launch_gemm_pq2(wb, dm, tokens, q, d, y, nullptr, as_stream(stream)));
 }
 
 int tq_group_dots(int fmt, const void* w, int64_t rows, int64_t cols, int64_t tokens, const int8_t* q,
@@ -184,7 +185,8 @@ int tq_group_dots(int fmt, const void* w, int64_t rows, int64_t cols, int64_t to
       return hip_status(tq::launch_gemv_pq2(wb, dm, q, nullptr, nullptr, idots, nullptr, as_stream(stream)));
     return hip_status(tq::launch_gemv_ptq1(wb, dm, q, nullptr, bsums, nullptr, idots, nullptr, as_stream(stream)));
   }
-  if (fmt != TQ_FMT_PQ2_0) return TQ_ERR_UNSUPPORTED;
+  if (fmt == TQ_FMT_PTQ1_0)
+    return hip_status(tq::launch_gemm_ptq1(wb, dm, tokens, q, nullptr, bsums, nullptr, idots, as_stream(stream)));
   return hip_status(tq::launch_gemm_pq2(wb, dm, tokens, q, nullptr, nullptr, idots, as_stream(stream)));
 }
 

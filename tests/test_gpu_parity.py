@@ -67,7 +67,7 @@ def gpu_pipeline(tq, fmt, W, x):
     T = x.shape[0]
     Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
     q, d, bs = tq.quantize_q8k(dev(x))
-    y = tq.gemm(fmt, Wd, R, K, q, d, bs) if T > 1 or fmt == "pq2_0" else tq.gemv(fmt, Wd, R, K, q, d, bs).view(1, R)
+    y = tq.gemm(fmt, Wd, R, K, q, d, bs) if T > 1 else tq.gemv(fmt, Wd, R, K, q, d, bs).view(1, R)
     I = tq.group_dots(fmt, Wd, R, K, q, bs)
     return Wd, host(q), host(d), host(bs), host(y).reshape(T, R), host(I)
 
@@ -204,49 +204,53 @@ def test_gemv_grid(tq, orc, fmt):
 GEMM_T = [2, 3, 4, 5, 7, 8, 16, 17, 33, 64, 65, 100]
 
 
+@pytest.mark.parametrize("fmt", ["pq2_0", "ptq1_0"])
 @pytest.mark.parametrize("R,K", [(1, 256), (33, 1280), (64, 2048), (130, 512)])
-def test_gemm_grid(tq, orc, R, K):
-    g = TI.rng(77, 6, R, K)
-    W = TI.pq2_matrix(g, R, K)
+def test_gemm_grid(tq, orc, fmt, R, K):
+    g = TI.rng(77, 6, R, K) if fmt == "pq2_0" else TI.rng(77, 16, R, K)
+    W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
     exact = total = 0
     for T in GEMM_T:
-        say("gemm", R, K, T)
+        say("gemm", fmt, R, K, T)
         x = TI.activations(g, T, K)
-        Wd, q, d, bs, y, I = gpu_pipeline(tq, "pq2_0", W, x)
+        Wd, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
         qo, do, _ = orc.quantize_q8k(x)
         assert np.array_equal(q, qo) and np.array_equal(d, do)
-        assert np.array_equal(I, orc.group_dots("pq2_0", W, qo)), (R, K, T)
-        yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
-        exact += assert_close_rows(y, yo, mag, what=f"gemm {R}x{K} T={T}")
+        assert np.array_equal(I, orc.group_dots(fmt, W, qo)), (R, K, T)
+        yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+        exact += assert_close_rows(y, yo, mag, what=f"gemm {fmt} {R}x{K} T={T}")
         total += y.size
         # one matrix-vector product per token gives the same outputs
         qd, dd, bd = tq.quantize_q8k(dev(x))
         for t in (0, T - 1):
-            yv = host(tq.gemv("pq2_0", Wd, R, K, qd[t], dd[t]))
+            yv = host(tq.gemv(fmt, Wd, R, K, qd[t], dd[t], bd[t]))
             assert_close_rows(yv, yo[t], mag[t], what=f"gemv token {t}")
-    say(f"gemm {R}x{K}: {exact}/{total} outputs bit-identical to the oracle")
+    say(f"gemm {fmt} {R}x{K}: {exact}/{total} outputs bit-identical to the oracle")
 
 
+@pytest.mark.parametrize("fmt", ["pq2_0", "ptq1_0"])
 @pytest.mark.parametrize("R,K", [(64, 256), (130, 1280), (200, 2048), (65, 3328), (17408, 5120)])
-def test_gemm_equals_stacked_gemv(tq, R, K):
+def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
     """A prompt product of T tokens gives, bit for bit, the outputs of T
-    matrix-vector products without a workspace: both round each group pair's
-    inner sum once and sum the superchunks in the same runs and run order.
-    The column counts give runs of 1, 2, 2, 4 and 5 superchunks with ragged
-    last runs; 17408x5120 is the prefill shape."""
+    matrix-vector products without a workspace.  pq2_0: both round each group
+    pair's inner sum once and sum the superchunks in the same runs and run
+    order; the column counts give runs of 1, 2, 2, 4 and 5 superchunks with
+    ragged last runs.  ptq1_0: every token of a block takes the one-token
+    kernel's steps (blocks of 1, 2, 4 or 8 tokens, the last one padded).
+    17408x5120 is the prefill shape."""
     import torch
 
     g = TI.rng(77, 15, R, K)
-    W = TI.pq2_matrix(g, R, K)
-    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+    Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
     for T in (2, 3, 4, 5, 6, 7, 8, 17, 64):
-        say("gemm vs gemv", R, K, T)
+        say("gemm vs gemv", fmt, R, K, T)
         x = TI.activations(g, T, K)
         q, d, bs = tq.quantize_q8k(dev(x))
-        y = host(tq.gemm("pq2_0", Wd, R, K, q, d, bs))
-        yv = np.stack([host(tq.gemv("pq2_0", Wd, R, K, q[t], d[t])) for t in range(T)])
+        y = host(tq.gemm(fmt, Wd, R, K, q, d, bs))
+        yv = np.stack([host(tq.gemv(fmt, Wd, R, K, q[t], d[t], bs[t])) for t in range(T)])
         assert np.array_equal(y, yv), (R, K, T, int(np.sum(y != yv)))
-        if T <= 8:
+        if T <= 8 and fmt == "pq2_0":
             yf = np.stack([host(tq.gemv_f32("pq2_0", Wd, R, K, dev(x[t]))) for t in range(T)])
             assert np.array_equal(y, yf), (R, K, T, "fused")
     del Wd
@@ -262,7 +266,8 @@ def test_gemv_workspace_split(tq, orc, fmt):
     over several workgroups; every output still matches the oracle, the
     arrival counters are back at zero after each call, and a second call
     gives the same bits, also after a call of another shape in between that
-    shares the workspace."""
+    shares the workspace.  ptq1_0 sums in one order whatever the split, so
+    its outputs equal those without a workspace."""
     import torch
 
     g = TI.rng(77, 12, 1 if fmt == "pq2_0" else 2)
@@ -281,6 +286,9 @@ def test_gemv_workspace_split(tq, orc, fmt):
             host(tq.gemv(*prev, ws=ws))
         y2 = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
         assert np.array_equal(y1, y2)
+        if fmt == "ptq1_0":
+            # one summation order for every split: the same bits without a workspace
+            assert np.array_equal(y1, host(tq.gemv(fmt, Wd, R, K, q, d, bs)))
         qo, do, _ = orc.quantize_q8k(x)
         yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
         assert_close_rows(y1, yo[0], mag[0], what=f"{fmt} {R}x{K} workspace")
@@ -492,6 +500,22 @@ def test_gemm_long_rows(tq, orc, R, K, T):
     assert np.array_equal(I, orc.group_dots("pq2_0", W, qo))
     yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
     assert_close_rows(y, yo, mag, what=f"gemm {R}x{K} T={T}")
+
+
+@pytest.mark.parametrize("R,K,T", [(3, 32768, 3), (70, 16384, 5), (64, 8192, 9)])
+def test_gemm_ptq1_token_blocks(tq, orc, R, K, T):
+    """ptq1_0 prompt products where the tables of a token block fill the LDS
+    budget: one token per block at the column limit, two at 16384 columns,
+    four at 8192 (with a padded last block)."""
+    g = TI.rng(77, 17, R, K)
+    W = TI.ptq1_matrix(g, R, K)
+    x = TI.activations(g, T, K)
+    say("gemm ptq1 token blocks", R, K, T)
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, "ptq1_0", W, x)
+    qo, do, _ = orc.quantize_q8k(x)
+    assert np.array_equal(I, orc.group_dots("ptq1_0", W, qo))
+    yo, mag = orc.matmul("ptq1_0", W, qo, do, with_mag=True)
+    assert_close_rows(y, yo, mag, what=f"gemm ptq1 {R}x{K} T={T}")
 
 
 def test_max_columns(tq, orc):

@@ -29,7 +29,7 @@ import numpy as np
 SEED_BASE = 20261202
 
 # Workload ids used in seeds.
-TINY, DECODE, PREFILL, STEP64, PTQ1 = 1, 2, 3, 4, 5
+TINY, DECODE, PREFILL, STEP64, PTQ1, PTQ1_PREFILL = 1, 2, 3, 4, 5, 6
 
 # The 81 bytes whose four 2-bit fields all lie in {0, 1, 2}.  Drawing a byte
 # uniformly from this list draws its four codes independently and uniformly.
@@ -114,6 +114,8 @@ def workload(name: str):
         "prefill_17408x5120_t4": ("pq2_0", 17408, 5120, 4, PREFILL),
         "prefill_17408x5120_t64": ("pq2_0", 17408, 5120, 64, PREFILL),
         "ptq1_32768x8192": ("ptq1_0", 32768, 8192, 1, PTQ1),
+        "ptq1_prefill_17408x5120_t4": ("ptq1_0", 17408, 5120, 4, PTQ1_PREFILL),
+        "ptq1_prefill_17408x5120_t64": ("ptq1_0", 17408, 5120, 64, PTQ1_PREFILL),
     }
     return table[name]
 
