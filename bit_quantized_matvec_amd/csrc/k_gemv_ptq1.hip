@@ -11,9 +11,12 @@
 //     superblock (1.75 bits per weight, bytes only reordered by the repack);
 //   * the four bytes of a code dword are split into two pairs of 16-bit lanes
 //     (bytes 0, 2 and bytes 1, 3), so one 32-bit multiply-by-3 advances two
-//     bytes at once without carries between them; after it the high byte of
-//     each lane is that byte's trit, and one v_perm_b32 gathers the four into
-//     a dword = one dot4 operand;
+//     bytes at once without carries between them, and one v_perm_b32 gathers
+//     the four high bytes into a dword = one dot4 operand.  Without masking
+//     between the multiplications the high byte after j + 1 of them is
+//     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1) (summation by
+//     parts turns the trit dot into h dots against the activations and their
+//     next-trit neighbours);
 //   * the trits are w + 1, so I = dot(t, q) - sum(q), the group sum coming
 //     from the q8_K partial sums (page 1, "the trick with 4 and 16": sum(y)
 //     over 128 values is one add over 8 partial sums);
@@ -191,9 +194,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       const uint32_t dws[13] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z,
                                 cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
                                 gp == 0 ? left.x : gp == 1 ? left.y : gp == 2 ? left.z : left.w};
-      int ia[NT], ib[NT];  // groups 2 gp and 2 gp + 1, per token
+      // groups 2 gp (a) and 2 gp + 1 (b), per token: i = sum h x + t4 x4 and
+      // j = sum h x_next, the group's dot(t, q) being i - 3 j
+      int ia[NT], ib[NT], ja[NT], jb[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) ia[n] = ib[n] = 0;
+      for (int n = 0; n < NT; ++n) ia[n] = ib[n] = ja[n] = jb[n] = 0;
       // Table entries of dword m: 5 levels (10 level-halves for the leftover
       // dword m = 12) x NT tokens, entry (level, token) at te[level * NT + token].
       // With one token all reads of a dword are issued together and the
@@ -203,6 +208,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       // are held in registers.
       constexpr int kLev = 5 * NT, kLeft = 10 * NT;
       constexpr bool kAll = NT == 1;
+      // With one or two tokens summation by parts (below) saves VALU; with
+      // more, its extra dot per level and token outweighs the masks it saves.
+      constexpr bool kParts = NT <= 2;
       auto te_off = [&](int m) { return m < 12 ? (12 * gp + m) * 8 * NT : (48 * 8 + gp * 16) * NT; };
       uint32_t tnext[kLeft];
       if constexpr (!kAll) {
@@ -228,32 +236,71 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
             else lds_run<kLeft>(tb + off, tnext);
           }
         }
-        uint32_t e = d & 0x00FF00FFu;
-        uint32_t o = (d >> 8) & 0x00FF00FFu;
+        // bytes 0, 2 and bytes 1, 3 of the code dword in 16-bit lanes
+        uint32_t e = __builtin_amdgcn_perm(0u, d, 0x0C020C00u);
+        uint32_t o = __builtin_amdgcn_perm(0u, d, 0x0C030C01u);
+        if (kParts && m < 12) {
+          // Summation by parts.  With h_j = floor(b 3^(j+1) / 256), the high
+          // byte of the 16-bit lane after j + 1 multiplications by 3 (b 3^5
+          // < 2^16, so nothing spills into the next lane), trit j is
+          // h_j - 3 h_(j-1).  Hence sum_j t_j x_j = sum_{j<4} h_j x_j
+          // - 3 sum_{j<3} h_j x_(j+1) + t_4 x_4, and h_0..h_3 <= 80 are valid
+          // signed dot4 operands: no masking between the multiplications.
+          uint32_t hprev = 0;
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
-          e *= 3u;
-          o *= 3u;
-          // each 16-bit lane now holds 3v < 768, so its high byte is the trit:
-          // one byte permute gathers the four (bytes 1, 3 of e and of o)
-          const int t = (int)__builtin_amdgcn_perm(o, e, 0x07030501u);
+          for (int j = 0; j < 5; ++j) {
+            e *= 3u;
+            o *= 3u;
+            const uint32_t hj = __builtin_amdgcn_perm(o, e, 0x07030501u);  // bytes 1, 3 of e and of o
+            if (j < 4) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (m < 6) {
-              ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ia[n], false);
-            } else if (m < 12) {
-              ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ib[n], false);
+              for (int n = 0; n < NT; ++n) {
+                int& a1 = m < 6 ? ia[n] : ib[n];
+                int& a3 = m < 6 ? ja[n] : jb[n];
+                a1 = __builtin_amdgcn_sdot4((int)hj, (int)tv[j * NT + n], a1, false);
+                if (j < 3) a3 = __builtin_amdgcn_sdot4((int)hj, (int)tv[(j + 1) * NT + n], a3, false);
+              }
             } else {
-              ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[2 * j * NT + n], ia[n], false);
-              ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[(2 * j + 1) * NT + n], ib[n], false);
+              // t_4 = h_4 - 3 h_3 byte by byte, without borrows (each byte is 0..2)
+              const int t4 = (int)(hj - 3u * hprev);
+#pragma unroll
+              for (int n = 0; n < NT; ++n) {
+                int& a1 = m < 6 ? ia[n] : ib[n];
+                a1 = __builtin_amdgcn_sdot4(t4, (int)tv[4 * NT + n], a1, false);
+              }
             }
+            hprev = hj;
           }
-          e &= 0x00FF00FFu;
-          o &= 0x00FF00FFu;
+        } else {
+          // trit by trit: each 16-bit lane holds v < 256, after the
+          // multiplication 3v < 768 and its high byte is the trit; the mask
+          // keeps v_(j+1) = 3v mod 256 (the leftover dword pairs two groups)
+#pragma unroll
+          for (int j = 0; j < 5; ++j) {
+            e *= 3u;
+            o *= 3u;
+            const int t = (int)__builtin_amdgcn_perm(o, e, 0x07030501u);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              if (m < 6) {
+                ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ia[n], false);
+              } else if (m < 12) {
+                ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[j * NT + n], ib[n], false);
+              } else {
+                ia[n] = __builtin_amdgcn_sdot4(t, (int)tv[2 * j * NT + n], ia[n], false);
+                ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[(2 * j + 1) * NT + n], ib[n], false);
+              }
+            }
+            e &= 0x00FF00FFu;
+            o &= 0x00FF00FFu;
+          }
         }
         if constexpr (!kAll) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
+          for (int n = 0; n < NT; ++n) {
+            asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
+            if constexpr (kParts) asm volatile("" : "+v"(ja[n]), "+v"(jb[n]));
+          }
         }
       }
       const uint32_t s2 = gp == 0 ? sc8.x : gp == 1 ? sc8.y : gp == 2 ? sc8.z : sc8.w;
@@ -267,7 +314,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
             const int t = min(tok0 + n, tokens - 1);
             const int16_t* bs = bsums + t * K / 16 + (size_t)g * 8;
             const int qsum = bs[0] + bs[1] + bs[2] + bs[3] + bs[4] + bs[5] + bs[6] + bs[7];
-            const int I = (h ? ib[n] : ia[n]) - qsum;
+            const int I = (h ? ib[n] - 3 * jb[n] : ia[n] - 3 * ja[n]) - qsum;
             if (IDOTS) {
               if (row < rows && tok0 + n < tokens) idots[((size_t)t * rows + row) * G + g] = I;
             } else {
