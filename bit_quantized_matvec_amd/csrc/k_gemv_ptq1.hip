@@ -32,6 +32,8 @@
 //     superblock sums in superblock order.  Waves, column slices (with a
 //     workspace) and token blocks only change who computes which superblock
 //     sum, so every launch shape gives the same bits;
+//   * one token: up to 8 waves per workgroup, one superblock each where the
+//     columns allow;
 //   * a prompt of several tokens runs NT tokens per workgroup (NT = 1, 2, 4
 //     or 8): each code dword is decoded once and its trits meet the NT
 //     tokens' tables, whose entries are interleaved by token.
@@ -41,7 +43,6 @@ namespace tq {
 namespace {
 
 constexpr int kMaxWaves = 8;   // the kernel's limit
-constexpr int kPlanWaves = 4;  // what the one-token plan uses
 constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock and token
 constexpr int kTasks = 48 + 8;                  // table-building tasks per superblock and token
 constexpr int kMaxTokBlock = 8;                 // tokens per workgroup
@@ -385,9 +386,9 @@ GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
   }
   p.scw = (G8 + slices - 1) / slices;
   p.slices = (G8 + p.scw - 1) / p.scw;
-  // up to 4 waves (measured on 32768 x 8192: 4 waves of two superblocks each
-  // beat 8 waves of one, which cannot share a CU two workgroups at a time)
-  const int waves = p.scw < kPlanWaves ? p.scw : kPlanWaves;
+  // up to 8 waves of one or more superblocks (measured on 32768 x 8192: 8
+  // waves of one superblock, 19.4 us, beat 4 waves of two, 20.8 us)
+  const int waves = p.scw < kMaxWaves ? p.scw : kMaxWaves;
   p.spw = (p.scw + waves - 1) / waves;
   p.waves = (p.scw + p.spw - 1) / p.spw;
   return p;
@@ -448,12 +449,9 @@ int ptq1_token_block(const Dims& dm, int64_t tokens) {
 
 hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                             const int16_t* bsums, float* y, int32_t* idots, hipStream_t s) {
-  // one workgroup per tile and token block, up to 8 waves of one or more
-  // superblocks each (the summation order does not depend on the split)
-  GemvPlan p = plan_gemv_ptq1(dm, false);
-  const int waves = p.scw < kMaxWaves ? p.scw : kMaxWaves;
-  p.spw = (p.scw + waves - 1) / waves;
-  p.waves = (p.scw + p.spw - 1) / p.spw;
+  // one workgroup per tile and token block, with the one-token plan's waves
+  // (the summation order does not depend on the split)
+  const GemvPlan p = plan_gemv_ptq1(dm, false);
   const int nt = ptq1_token_block(dm, tokens);
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
