@@ -89,9 +89,14 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 //
 // Task t < 48 (D = t) reads the 20 bytes q[g][20m .. 20m + 19] and writes
 // the five entries (D, 0..4), a 4 x 5 byte transpose; task 48 + 2p + h reads
-// q[g][120 .. 127] and writes the five entries (p, h, 0..4).  `qt` is the
-// token's row of q; `out` the superblock's table, `nt` tokens interleaved.
-__device__ __forceinline__ void build_task(const int8_t* __restrict__ qt, int G, int sb, int task, uint32_t* out,
+// q[g][120 .. 127] and writes the five entries (p, h, 0..4).  The spare
+// dwords 8D + 6 and 8D + 7 of D = 6 gi (m = 0) hold group gi's sum of q (the
+// sum of its 8 partial sums) and its d_x (as bits), so that the products
+// read nothing but LDS.  `qt`, `bst`, `dxt` are the token's rows of q, the
+// partial sums and d_x (dxt may be null: group dots only); `out` the
+// superblock's table, `nt` tokens interleaved.
+__device__ __forceinline__ void build_task(const int8_t* __restrict__ qt, const int16_t* __restrict__ bst,
+                                           const float* __restrict__ dxt, int G, int sb, int task, uint32_t* out,
                                            int nt) {
   auto byte = [](uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; };
   if (task < 48) {
@@ -101,6 +106,17 @@ __device__ __forceinline__ void build_task(const int8_t* __restrict__ qt, int G,
       const uint32_t* src = reinterpret_cast<const uint32_t*>(qt + (size_t)g * 128 + 20 * m);
 #pragma unroll
       for (int k = 0; k < 5; ++k) w[k] = src[k];
+    }
+    if (m == 0) {
+      int qsum = 0;
+      float d = 0.0f;
+      if (g < G) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qsum += bst[(size_t)g * 8 + k];
+        if (dxt) d = dxt[g >> 1];
+      }
+      out[(task * 8 + 6) * nt] = (uint32_t)qsum;
+      out[(task * 8 + 7) * nt] = __builtin_bit_cast(uint32_t, d);
     }
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
@@ -165,8 +181,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
     const int n = i % NT, r = i / NT;
     const int sb = wg0 + r / kTasks, task = r % kTasks;
     uint32_t* out = table + (size_t)(sb - wg0) * kTableDwords * NT + n;
-    if (tok0 + n < tokens) build_task(q + (size_t)(tok0 + n) * K, G, sb, task, out, NT);
-    else build_task(q, 0, sb, task, out, NT);  // padding token: G = 0 gives zero entries
+    if (tok0 + n < tokens) {
+      const size_t t = (size_t)(tok0 + n);
+      build_task(q + t * K, bsums + t * K / 16, dx ? dx + t * K / 256 : nullptr, G, sb, task, out, NT);
+    } else {
+      build_task(q, bsums, nullptr, 0, sb, task, out, NT);  // padding token: G = 0 gives zero entries
+    }
   }
   __syncthreads();
 
@@ -310,16 +330,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
         const int g = sb * 8 + 2 * gp + h;
         if (g < G) {
           const double dw = (double)half_bits_to_float(h ? (s2 >> 16) : (s2 & 0xffffu));
+          const uint32_t* gs = tb + (8 * 6 * (2 * gp + h) + 6) * NT;  // the group's sum of q, then d_x
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            const int t = min(tok0 + n, tokens - 1);
-            const int16_t* bs = bsums + t * K / 16 + (size_t)g * 8;
-            const int qsum = bs[0] + bs[1] + bs[2] + bs[3] + bs[4] + bs[5] + bs[6] + bs[7];
+            const int qsum = (int)gs[n];
             const int I = (h ? ib[n] - 3 * jb[n] : ia[n] - 3 * ja[n]) - qsum;
             if (IDOTS) {
-              if (row < rows && tok0 + n < tokens) idots[((size_t)t * rows + row) * G + g] = I;
+              if (row < rows && tok0 + n < tokens) idots[((size_t)(tok0 + n) * rows + row) * G + g] = I;
             } else {
-              acc[n] += (dw * (double)dx[t * K / 256 + (g >> 1)]) * (double)I;
+              acc[n] += (dw * (double)__builtin_bit_cast(float, gs[NT + n])) * (double)I;
             }
           }
         }
