@@ -265,6 +265,21 @@ def step64_bench(torch, tq, reps):
             "weight_bytes": wbytes, "two_kernel_ms_per_token": g2_s * 1e3 / reps}
 
 
+def tiny_bench(torch, tq, K):
+    """The 256x1024 workload: one fused call per step, replayed from a graph
+    (launch-bound: its 70 KB of weights stay in the caches)."""
+    fmt, Wc, x = TI.make("tiny_256x1024")
+    R, G, _ = Wc.shape
+    C = G * 128
+    W = tq.repack(torch.from_numpy(Wc.reshape(-1)).cuda(), fmt, R, C)
+    xd = torch.from_numpy(x[0].copy()).cuda()
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+    ws = tq.workspace(fmt, R, C, 1)
+    step = lambda i: tq.gemv_f32(fmt, W, R, C, xd, out=y, ws=ws)
+    t = graph_time(torch, step, K)
+    return {"rows": R, "cols": C, "us_per_step": t * 1e6 / K, "gweights_s": R * C * K / t / 1e9}
+
+
 def quantize_bench(torch, tq, K):
     C = 8192
     xs = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 2), 1, C)).cuda()
@@ -274,7 +289,9 @@ def quantize_bench(torch, tq, K):
         tq.quantize_q8k(xs, out=out)
     torch.cuda.synchronize()
     us = batch_us(torch, lambda i: tq.quantize_q8k(xs, out=out), K)
-    return {"cols": C, "us": us}
+    # replayed from a graph: the kernel's cadence without the host's launch cost
+    graph_us = graph_time(torch, lambda i: tq.quantize_q8k(xs, out=out), K) * 1e6 / K
+    return {"cols": C, "us": us, "graph_us": graph_us}
 
 
 def ceiling_probe(torch):
@@ -446,6 +463,7 @@ def main():
             p = prefill_bench(torch, tq, T, 100, "ptq1_0")
             extra[f"ptq1_prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
         extra["quantize_8192"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in quantize_bench(torch, tq, 200).items()}
+        extra["tiny_256x1024"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in tiny_bench(torch, tq, 1000).items()}
         extra["ceiling"] = {k: round(v, 1) for k, v in ceiling_probe(torch).items()}
     out["extra"] = extra
     if not args.no_cpu:

@@ -98,7 +98,7 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
                                               const int* __restrict__ q, const float* __restrict__ dx,
                                               const float4* __restrict__ xf, float* __restrict__ y,
                                               int32_t* __restrict__ idots, int rows, int nsc, int G8, int scw, int spw,
-                                              double* __restrict__ partials, unsigned* __restrict__ counters, int tile,
+                                              uint8_t* __restrict__ ws, int tile,
                                               int ptile) {
   __shared__ double red[kMaxWaves][64];
   const int lane = threadIdx.x & 63;
@@ -262,20 +262,21 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   // The partial goes out with an agent-scope atomic store (written through
   // to the level shared by all XCDs, so no whole-L2 write-back is needed);
   // the counter is bumped only after the store has completed (vmcnt = 0).
-  __hip_atomic_store(&partials[((size_t)ptile * nslices + slice) * 64 + lane], s, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  double* partials = ws_partials(ws, ptile);
+  unsigned* counter = ws_counter(ws, ptile);
+  __hip_atomic_store(&partials[slice * 64 + lane], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&counters[ptile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0, 64);
   if (prev != (unsigned)(nslices - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   double t = 0.0;
   for (int k = 0; k < nslices; ++k)
-    t += __hip_atomic_load(&partials[((size_t)ptile * nslices + k) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t += __hip_atomic_load(&partials[k * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (row < rows) y[row] = (float)t;
-  if (lane == 0) __hip_atomic_store(&counters[ptile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int RING, bool IDOTS, bool NT, bool LDSQ, bool FX, int XB = 1>
@@ -285,23 +286,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
                                                                   const float4* __restrict__ xf,
                                                                   float* __restrict__ y, int32_t* __restrict__ idots,
                                                                   int rows, int nsc, int G8, int scw, int spw,
-                                                                  double* __restrict__ partials, unsigned* __restrict__ counters) {
-  gemv_pq2_body<RING, IDOTS, NT, LDSQ, FX, XB>(codes, scales, q, dx, xf, y, idots, rows, nsc, G8, scw, spw, partials,
-                                               counters, blockIdx.x, blockIdx.x);
+                                                                  uint8_t* __restrict__ ws) {
+  gemv_pq2_body<RING, IDOTS, NT, LDSQ, FX, XB>(codes, scales, q, dx, xf, y, idots, rows, nsc, G8, scw, spw, ws,
+                                               blockIdx.x, blockIdx.x);
 }
 
 // Several independent fused products with the same column count in one
 // launch: workgroup x belongs to problem m with tile0[m] <= x < tile0[m + 1].
 template <int XB>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_batch_kernel(GemvBatch b, int nsc, int G8, int scw, int spw,
-                                                                        double* __restrict__ partials,
-                                                                        unsigned* __restrict__ counters) {
+                                                                        uint8_t* __restrict__ ws) {
   const int x = blockIdx.x;
   int m = 0;
 #pragma unroll
   for (int k = 1; k < kMaxBatch; ++k) m += (k < b.n && x >= b.tile0[k]) ? 1 : 0;
   gemv_pq2_body<2, false, true, true, true, XB>(b.codes[m], b.scales[m], nullptr, nullptr, b.x[m], b.y[m], nullptr,
-                                                b.rows[m], nsc, G8, scw, spw, partials, counters, x - b.tile0[m], x);
+                                                b.rows[m], nsc, G8, scw, spw, ws, x - b.tile0[m], x);
 }
 
 GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace) {
@@ -333,9 +333,7 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   const int nsc = (int)dm.nsc;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
-  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
-  double* partials =
-      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   // one slice's activations are staged in LDS when they fit (always with the
   // column splits a workspace allows for matrices of up to 128 Ki columns)
@@ -347,7 +345,7 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   const int pieces = (p.scw * 16 + 64 * p.waves - 1) / (64 * p.waves);
 #define TQ_LAUNCH(ID, LQ, XB)                                                                                     \
   hipLaunchKernelGGL((gemv_pq2_kernel<kRing, ID, true, LQ, false, XB>), grid, block, LQ ? (unsigned)stage : 0u, s, \
-                     codes, scales, qi, dx, nullptr, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, partials, counters)
+                     codes, scales, qi, dx, nullptr, y, idots, (int)dm.rows, nsc, ns, p.scw, p.spw, ws)
 #define TQ_LAUNCH_Q(ID)                          \
   if (!ldsq) TQ_LAUNCH(ID, false, 1);            \
   else if (pieces <= 1) TQ_LAUNCH(ID, true, 1);  \
@@ -377,16 +375,14 @@ hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* 
   if (stage > kMaxStageBytes) return hipErrorInvalidValue;  // the caller checks gemv_pq2_fused_fits first
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
-  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
-  double* partials =
-      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   // quantization batch: the blocks one wave quantizes (no more than 8 at once)
   const int per_wave = (p.scw + p.waves - 1) / p.waves;
 #define TQ_LAUNCH(XB)                                                                                             \
   hipLaunchKernelGGL((gemv_pq2_kernel<kRing, false, true, true, true, XB>), grid, block, (unsigned)stage, s, codes, \
                      scales, nullptr, nullptr, reinterpret_cast<const float4*>(x), y, nullptr, (int)dm.rows,        \
-                     (int)dm.nsc, (int)dm.G8, p.scw, p.spw, partials, counters)
+                     (int)dm.nsc, (int)dm.G8, p.scw, p.spw, ws)
   if (per_wave <= 2) TQ_LAUNCH(2);
   else if (per_wave <= 4) TQ_LAUNCH(4);
   else TQ_LAUNCH(8);
@@ -398,14 +394,12 @@ hipError_t launch_gemv_pq2_fused_batch(const GemvBatch& b, const Dims& dm, void*
   const GemvPlan p = plan_gemv_pq2(dm, workspace != nullptr);
   const size_t stage = (size_t)p.scw * (256 + 4);
   if (stage > kMaxStageBytes) return hipErrorInvalidValue;  // the caller checks gemv_pq2_fused_fits first
-  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
-  double* partials =
-      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   const int per_wave = (p.scw + p.waves - 1) / p.waves;
 #define TQ_LAUNCH(XB)                                                                                                 \
   hipLaunchKernelGGL(gemv_pq2_batch_kernel<XB>, grid, block, (unsigned)stage, s, b, (int)dm.nsc, (int)dm.G8, p.scw, \
-                     p.spw, partials, counters)
+                     p.spw, ws)
   if (per_wave <= 2) TQ_LAUNCH(2);
   else if (per_wave <= 4) TQ_LAUNCH(4);
   else TQ_LAUNCH(8);

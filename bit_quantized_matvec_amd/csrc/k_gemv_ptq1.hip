@@ -160,8 +160,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
                                                                    const int8_t* __restrict__ q, const float* __restrict__ dx,
                                                                    const int16_t* __restrict__ bsums, float* __restrict__ y,
                                                                    int32_t* __restrict__ idots, int rows, int G, int G8,
-                                                                   int scw, int spw, double* __restrict__ partials,
-                                                                   unsigned* __restrict__ counters, int tokens) {
+                                                                   int scw, int spw, uint8_t* __restrict__ ws,
+                                                                   int tokens) {
   extern __shared__ __align__(16) uint32_t table[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -375,21 +375,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
   // shared by all XCDs, so no whole-L2 write-back is needed); the counter is
   // bumped only after the stores have completed (vmcnt = 0).  The last
   // workgroup to arrive adds all the tile's superblock sums in order.
+  double* partials = ws_partials(ws, tile);
+  unsigned* counter = ws_counter(ws, tile);
   for (int sb = wg0; sb < wg1; ++sb)
-    __hip_atomic_store(&partials[((size_t)tile * G8 + sb) * 64 + lane], sb_sum(sb, 0), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&partials[sb * 64 + lane], sb_sum(sb, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0, 64);
   if (prev != (unsigned)(nslices - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  double t = __hip_atomic_load(&partials[(size_t)tile * G8 * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  double t = __hip_atomic_load(&partials[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int sb = 1; sb < G8; ++sb)
-    t += __hip_atomic_load(&partials[((size_t)tile * G8 + sb) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t += __hip_atomic_load(&partials[sb * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (row < rows) y[row] = (float)t;
-  if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace) {
@@ -418,21 +419,19 @@ namespace {
 template <bool IDOTS, int NT>
 void launch_ptq1(const dim3& grid, const dim3& block, size_t lds, hipStream_t s, const uint4* codes,
                  const uint4* scales, const int8_t* q, const float* dx, const int16_t* bsums, float* y, int32_t* idots,
-                 const Dims& dm, const GemvPlan& p, double* partials, unsigned* counters, int tokens) {
+                 const Dims& dm, const GemvPlan& p, uint8_t* ws, int tokens) {
   hipLaunchKernelGGL((gemv_ptq1_kernel<IDOTS, NT>), grid, block, lds, s, codes, scales, q, dx, bsums, y, idots,
-                     (int)dm.rows, (int)dm.G, (int)dm.G8, p.scw, p.spw, partials, counters, tokens);
+                     (int)dm.rows, (int)dm.G, (int)dm.G8, p.scw, p.spw, ws, tokens);
 }
 
 template <int NT>
 void launch_ptq1_nt(bool idots_out, const dim3& grid, const dim3& block, size_t lds, hipStream_t s,
                     const uint4* codes, const uint4* scales, const int8_t* q, const float* dx, const int16_t* bsums,
-                    float* y, int32_t* idots, const Dims& dm, const GemvPlan& p, double* partials, unsigned* counters,
-                    int tokens) {
+                    float* y, int32_t* idots, const Dims& dm, const GemvPlan& p, uint8_t* ws, int tokens) {
   if (idots_out)
-    launch_ptq1<true, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, partials, counters, tokens);
+    launch_ptq1<true, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, ws, tokens);
   else
-    launch_ptq1<false, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, partials, counters,
-                           tokens);
+    launch_ptq1<false, NT>(grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, ws, tokens);
 }
 
 }  // namespace
@@ -442,12 +441,10 @@ hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t*
                                  hipStream_t s) {
   const uint4* codes = reinterpret_cast<const uint4*>(w);
   const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
-  unsigned* counters = reinterpret_cast<unsigned*>(workspace);
-  double* partials =
-      workspace ? reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_counter_bytes(dm)) : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   launch_ptq1_nt<1>(idots != nullptr, grid, block, ptq1_lds_bytes(p.scw, 1), s, codes, scales, q, dx, bsums, y, idots,
-                    dm, p, partials, counters, 1);
+                    dm, p, ws, 1);
   return hipGetLastError();
 }
 
@@ -479,10 +476,10 @@ hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, co
   const bool io = idots != nullptr;
   const int T = (int)tokens;
   switch (nt) {
-    case 1: launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
-    case 2: launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
-    case 4: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
-    default: launch_ptq1_nt<8>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, nullptr, T); break;
+    case 1: launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
+    case 2: launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
+    case 4: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
+    default: launch_ptq1_nt<8>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
   }
   return hipGetLastError();
 }

@@ -19,14 +19,20 @@ constexpr int kMaxSlices = 16;
 // 3:0 and 15:14 = 0; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Workspace of the split products: per-tile arrival counters (zero between
-// calls), then fp64 partial sums, [tile][slice][64] for pq2_0 and
-// [tile][superblock][64] for ptq1_0.
-inline int64_t workspace_counter_bytes(const Dims& d) { return (d.ntiles * 4 + 255) / 256 * 256; }
-inline int64_t workspace_bytes(const Dims& d, bool ptq1) {
-  const int64_t per_tile = ptq1 && d.G8 > kMaxSlices ? d.G8 : kMaxSlices;
-  return workspace_counter_bytes(d) + d.ntiles * per_tile * 64 * 8;
+// Workspace of the split products: one block of kWsTileBytes per 64-row
+// tile (the global tile index of a batch), at the same place for every shape,
+// format and entry point, so that one workspace serves any later call whose
+// tiles it covers: the tile's arrival counter (zero between calls; 16 bytes
+// with padding), then room for 32 x 64 fp64 partial sums -- [slice][row] for
+// pq2_0 (up to 16 slices), [superblock][row] for ptq1_0 (up to 32).
+constexpr int64_t kWsTileBytes = 16 + 32 * 64 * 8;
+__host__ __device__ inline unsigned* ws_counter(uint8_t* ws, int64_t tile) {
+  return reinterpret_cast<unsigned*>(ws + tile * kWsTileBytes);
 }
+__host__ __device__ inline double* ws_partials(uint8_t* ws, int64_t tile) {
+  return reinterpret_cast<double*>(ws + tile * kWsTileBytes + 16);
+}
+inline int64_t workspace_bytes(const Dims& d) { return d.ntiles * kWsTileBytes; }
 
 hipError_t launch_quantize_q8k(const float* x, int64_t nblocks, int8_t* q, float* d, int16_t* bsums, hipStream_t s);
 

@@ -100,7 +100,7 @@ int tq_quantize_q8k(const float* x, int64_t tokens, int64_t cols, int8_t* q, flo
 
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens) {
   if (shape_status(fmt, rows, cols, tokens) != TQ_OK) return 0;
-  return tq::workspace_bytes(tq::dims(rows, cols), fmt == TQ_FMT_PTQ1_0);
+  return tq::workspace_bytes(tq::dims(rows, cols));
 }
 
 int tq_gemv(int fmt, const void* w, int64_t rows, int64_t cols, const int8_t* q, const float* d, const int16_t* bsums,

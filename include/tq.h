@@ -111,14 +111,14 @@ int tq_quantize_q8k(const float *x, int64_t tokens, int64_t cols, int8_t *q, flo
  * 64-row tile (fp64 partial sums plus per-tile arrival counters), which keeps
  * all compute units busy when the row count is small and balances the load
  * when it is large.  Contract: device memory of at least this size, 16-byte
- * aligned, zero-filled once before its first use.  It starts with one 32-bit
- * arrival counter per 64-row tile (rounded up to 256 bytes), which every call
- * returns to zero; the fp64 partial sums after it are always written before
- * they are read and keep whatever the last call left.  So it can be reused
- * by later calls of any shape it is large enough for (also inside a
- * captured graph) without clearing.  Calls that run at the same time must
- * not share one.
- * Returns 0 for an invalid shape. */
+ * aligned, zero-filled once before its first use.  It holds one block of
+ * 16400 bytes per 64-row tile, laid out alike for every shape, format and
+ * entry point: the tile's 32-bit arrival counter, which every call returns to
+ * zero, then fp64 partial sums that are always written before they are read
+ * and keep whatever the last call left.  So it can be reused by later calls of
+ * any shape, format and token count whose tile count it covers (also inside a
+ * captured graph) without clearing.  Calls that run at the same time must not
+ * share one.  Returns 0 for an invalid shape. */
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens);
 
 /* Matrix-vector product, one token (page 1, "the trick with 4 and 16" and

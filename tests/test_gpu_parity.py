@@ -60,6 +60,17 @@ def assert_close_rows(y, ref, mag, rtol=1e-5, what=""):
     return int(np.sum(y == ref))
 
 
+def counters_clear(tq, ws, tiles):
+    """True when the arrival counters of the first `tiles` tiles are zero: each
+    tile's workspace block (the size of a one-tile workspace) starts with it."""
+    import torch
+
+    per = tq.workspace_bytes("pq2_0", 64, 256)
+    idx = torch.arange(tiles, device=ws.device) * per
+    words = torch.stack([ws[idx + k] for k in range(4)])
+    return int(torch.count_nonzero(words)) == 0
+
+
 def gpu_pipeline(tq, fmt, W, x):
     """Repack, quantize and multiply on the GPU; returns numpy results."""
     R, G, _ = W.shape
@@ -237,6 +248,7 @@ def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
     order; the column counts give runs of 1, 2, 2, 4 and 5 superchunks with
     ragged last runs.  ptq1_0: every token of a block takes the one-token
     kernel's steps (blocks of 1, 2, 4 or 8 tokens, the last one padded).
+    A workspace changes nothing (twice in a row, arrival counters at zero).
     17408x5120 is the prefill shape."""
     import torch
 
@@ -250,6 +262,12 @@ def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
         y = host(tq.gemm(fmt, Wd, R, K, q, d, bs))
         yv = np.stack([host(tq.gemv(fmt, Wd, R, K, q[t], d[t], bs[t])) for t in range(T)])
         assert np.array_equal(y, yv), (R, K, T, int(np.sum(y != yv)))
+        # with a workspace
+        ws = tq.workspace(fmt, R, K, T)
+        for _ in range(2):
+            yw = host(tq.gemm(fmt, Wd, R, K, q, d, bs, ws=ws))
+            assert np.array_equal(yw, y), (R, K, T, "workspace", int(np.sum(yw != y)))
+            assert counters_clear(tq, ws, -(-R // 64))
         if T <= 8 and fmt == "pq2_0":
             yf = np.stack([host(tq.gemv_f32("pq2_0", Wd, R, K, dev(x[t]))) for t in range(T)])
             assert np.array_equal(y, yf), (R, K, T, "fused")
@@ -281,7 +299,7 @@ def test_gemv_workspace_split(tq, orc, fmt):
         q, d, bs = tq.quantize_q8k(dev(x))
         assert tq.workspace_bytes(fmt, R, K) <= ws.numel()
         y1 = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
-        assert int(torch.count_nonzero(ws[: 4 * ((R + 63) // 64)])) == 0, "arrival counters not returned to zero"
+        assert counters_clear(tq, ws, (R + 63) // 64), "arrival counters not returned to zero"
         if prev is not None:
             host(tq.gemv(*prev, ws=ws))
         y2 = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
@@ -322,10 +340,47 @@ def test_gemv_f32_fused(tq, orc, R, K, use_ws):
     yq = host(tq.gemv("pq2_0", Wd, R, K, q, d, ws=ws))
     assert np.array_equal(yf, yq) and np.array_equal(yf, yf2)
     if ws is not None:
-        assert int(torch.count_nonzero(ws[: 4 * ((R + 63) // 64)])) == 0
+        assert counters_clear(tq, ws, (R + 63) // 64)
     qo, do, _ = orc.quantize_q8k(x)
     yo, mag = orc.matmul("pq2_0", W, qo, do, with_mag=True)
     assert_close_rows(yf, yo[0], mag[0], what=f"gemv_f32 {R}x{K}")
+
+
+def test_workspace_reuse_across_shapes(tq, orc):
+    """One workspace shared by split products of different tile counts (above
+    and below 64 tiles) and both formats, in an order where a call with fewer
+    tiles comes between two calls with more: every call's outputs match its
+    first result bit for bit and the oracle within tolerance, and all arrival
+    counters are back at zero after each call."""
+    import torch
+
+    g = TI.rng(77, 18)
+    shapes = [("pq2_0", 6000, 1024), ("pq2_0", 130, 512), ("ptq1_0", 5000, 2048), ("pq2_0", 4500, 2048),
+              ("ptq1_0", 100, 4096)]
+    cases = []
+    for fmt, R, K in shapes:
+        W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+        x = TI.activations(g, 1, K)
+        Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
+        q, d, bs = tq.quantize_q8k(dev(x))
+        qo, do, _ = orc.quantize_q8k(x)
+        yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+        cases.append((fmt, R, K, Wd, q, d, bs, yo[0], mag[0]))
+    tiles = max(-(-R // 64) for _, R, _ in shapes)
+    ws = tq.workspace("pq2_0", tiles * 64, 256)
+    first = {}
+    for rnd in range(2):
+        for i in [0, 1, 2, 3, 4, 0, 2, 1, 3]:
+            fmt, R, K, Wd, q, d, bs, yo, mag = cases[i]
+            say("workspace reuse", rnd, fmt, R, K)
+            assert tq.workspace_bytes(fmt, R, K) <= ws.numel()
+            y = host(tq.gemv(fmt, Wd, R, K, q, d, bs, ws=ws))
+            assert counters_clear(tq, ws, tiles), (fmt, R, K)
+            if i in first:
+                assert np.array_equal(y, first[i]), (fmt, R, K)
+            else:
+                first[i] = y
+                assert_close_rows(y, yo, mag, what=f"{fmt} {R}x{K} shared workspace")
 
 
 @pytest.mark.parametrize("rows,K", [([200, 333], 2560), ([64, 1, 130, 65], 1024), ([7000], 768), ([6000, 6000], 512)])
@@ -348,7 +403,7 @@ def test_gemv_f32_batch(tq, orc, rows, K):
     R64 = sum(-(-R // 64) * 64 for R in rows)
     ws = tq.workspace("pq2_0", R64, K)
     yw = [host(y) for y in tq.gemv_f32_batch("pq2_0", Wd, rows, K, xd, ws=ws)]
-    assert int(torch.count_nonzero(ws[: 4 * (R64 // 64)])) == 0
+    assert counters_clear(tq, ws, R64 // 64)
     for m, R in enumerate(rows):
         qo, do, _ = orc.quantize_q8k(xs[m])
         yo, mag = orc.matmul("pq2_0", Ws[m], qo, do, with_mag=True)
