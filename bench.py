@@ -376,27 +376,66 @@ def recorded_traffic():
     return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle on the host cores: quantize + product over the full
-    32768 x 8192 matrix, repeated while the wall budget lasts."""
+    32768 x 8192 matrix, repeated while the wall budget lasts.  Beside it, in
+    about a third of that budget each: the same on one core, the ptq1_0
+    32768 x 8192 product and the 17408 x 5120 prompt product at 64 tokens on
+    all cores (row samples, scaled to the whole matrix)."""
     import oracle
 
     oracle.build(force=False)
     fmt, Wc, x = TI.make("decode_32768x8192")
     R, G, _ = Wc.shape
     cores = len(os.sched_getaffinity(0))
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def run(call, budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            call()
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                return n, time.perf_counter() - t0
+
+    def full_pass():
         q, d, _ = oracle.quantize_q8k(x)
         oracle.matmul(fmt, Wc, q, d, threads=cores)
-        passes += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": passes * R * G * 128 / dt / 1e9, "unit": "Gweights/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} full passes (q8_K quantize + 32768x8192 pq2_0 product, fp64 epilogue) over {dt:.1f} s, "
-                      f"row ranges split over {cores} threads"}
+
+    passes, dt = run(full_pass, seconds)
+    out = {"value": passes * R * G * 128 / dt / 1e9, "unit": "Gweights/s", "cores": cores, "kind": "oracle",
+           "sample": f"{passes} full passes (q8_K quantize + 32768x8192 pq2_0 product, fp64 epilogue) over {dt:.1f} s, "
+                     f"row ranges split over {cores} threads",
+           "cpu": _cpu_model(), "cflags": " ".join(oracle.CFLAGS)}
+    side = seconds / 3
+    # one core, the first 4096 rows of the same product
+    q1, d1, _ = oracle.quantize_q8k(x)
+    n, dt = run(lambda: oracle.matmul(fmt, Wc, q1, d1, rows=(0, 4096), threads=1), side)
+    out["one_core_gweights_s"] = n * 4096 * G * 128 / dt / 1e9
+    # ptq1_0 32768 x 8192 on all cores
+    pfmt, Pc, px = TI.make("ptq1_32768x8192")
+    pq, pd, _ = oracle.quantize_q8k(px)
+    n, dt = run(lambda: oracle.matmul(pfmt, Pc, pq, pd, threads=cores), side)
+    out["ptq1_gweights_s"] = n * Pc.shape[0] * Pc.shape[1] * 128 / dt / 1e9
+    del Pc
+    # prompt product 17408 x 5120, 64 tokens, a block of 1024 rows on all cores
+    gfmt, Gc, gx = TI.make("prefill_17408x5120_t64")
+    gq, gd, _ = oracle.quantize_q8k(gx)
+    sub = np.ascontiguousarray(Gc[:1024])
+    n, dt = run(lambda: oracle.matmul(gfmt, sub, gq, gd, threads=cores), side)
+    out["prefill_t64_gmac_s"] = n * 1024 * Gc.shape[1] * 128 * gx.shape[0] / dt / 1e9
+    return out
 
 
 def main():
