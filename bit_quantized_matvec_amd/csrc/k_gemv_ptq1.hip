@@ -14,9 +14,10 @@
 //     bytes at once without carries between them, and one v_perm_b32 gathers
 //     the four high bytes into a dword = one dot4 operand.  Without masking
 //     between the multiplications the high byte after j + 1 of them is
-//     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1) (summation by
-//     parts turns the trit dot into h dots against the activations and their
-//     next-trit neighbours);
+//     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1): with one or
+//     two tokens, summation by parts turns the trit dot into h dots against
+//     the activations and their next-trit neighbours (no masks); with more
+//     tokens each trit is masked out and dotted once per token;
 //   * the trits are w + 1, so I = dot(t, q) - sum(q), the group sum coming
 //     from the q8_K partial sums (page 1, "the trick with 4 and 16": sum(y)
 //     over 128 values is one add over 8 partial sums);
@@ -26,7 +27,10 @@
 //     dword: a 4 x 5 byte transpose), and the main loop reads it with
 //     wave-uniform (broadcast) LDS loads.  The two bytes per group that do
 //     not fill a dword are paired with the next group's, and their padding
-//     trits meet zero activations;
+//     trits meet zero activations.  The table also holds each group's sum of
+//     q and its d_x, so the products read nothing but LDS (scalar loads in
+//     the loop would make every LDS wait a full one: they return out of
+//     order);
 //   * the fp64 sum has one fixed order whatever the launch: the terms of a
 //     superblock's 8 groups are added in group order from zero, and the
 //     superblock sums in superblock order.  Waves, column slices (with a
