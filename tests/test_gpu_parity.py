@@ -154,6 +154,69 @@ def test_repack_flags_code_3(tq):
         tq.repack(dev(W.reshape(-1)), "pq2_0", 70, 512)
 
 
+def integer_activations(g, T, K):
+    """Integer activations in [-127, 127] with |x| = 127 at a random place of
+    every 256-block, so that q8_K reproduces them exactly (d = 1, q = x): the
+    pages' integer-oracle inputs, with amax forced in every block, not just
+    the first (page 1, "what didn't work": the first run failed for that)."""
+    x = g.integers(-127, 128, size=(T, K)).astype(np.float32)
+    for t in range(T):
+        for b in range(K // 256):
+            x[t, 256 * b + int(g.integers(0, 256))] = 127.0 if g.integers(0, 2) else -127.0
+    return x
+
+
+def check_integer_case(tq, orc, fmt, W, x, what):
+    """q8_K of x is x itself; the integer group dots equal a plain int64 numpy
+    product of the decoded weights and x; y is within R15 of the fp64 sum of
+    d_w * I (d_x = 1)."""
+    R, G, _ = W.shape
+    K = G * 128
+    T = x.shape[0]
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+    assert np.array_equal(q, x.astype(np.int8)) and np.all(d == 1.0), what
+    assert np.array_equal(bs, x.reshape(T, K // 16, 16).sum(axis=2).astype(np.int16)), what
+    w, dw, _ = orc.decode(fmt, W)
+    Iref = np.einsum("rgk,tgk->trg", w.astype(np.int64).reshape(R, G, 128), x.astype(np.int64).reshape(T, G, 128))
+    assert np.array_equal(I, Iref), what
+    terms = dw.astype(np.float64)[None, :, :] * Iref
+    yref = terms.sum(axis=2)
+    assert_close_rows(y, yref, np.abs(terms).sum(axis=2), what=what)
+
+
+@pytest.mark.parametrize("fmt", ["pq2_0", "ptq1_0"])
+def test_integer_grid(tq, orc, fmt):
+    """The pages' integer-oracle grid (page 1, "did i break the model?": batch
+    widths 1-5, 7, 8; rows 4, 8, 12; inner sizes 256, 512, 1024), 63 shapes per
+    format, plus extremes: every activation +-127 against all-+1 and all--1
+    weights (|I| = 128 * 127, the largest group dot) and all-zero weights."""
+    g = TI.rng(77, 19, 1 if fmt == "pq2_0" else 2)
+    n = 0
+    for T in (1, 2, 3, 4, 5, 7, 8):
+        for R in (4, 8, 12):
+            for K in (256, 512, 1024):
+                W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+                check_integer_case(tq, orc, fmt, W, integer_activations(g, T, K), f"{fmt} T={T} R={R} K={K}")
+                n += 1
+    R, K, T = 12, 1024, 5
+    sc = TI.scales_f16(g, R, K)
+    ones = 0xAA if fmt == "pq2_0" else 255  # every weight +1 (code 2 / trits 2,2,2,2,2)
+    negs = 0x00  # every weight -1 (code 0 / trits 0)
+    for byte, sign in ((ones, 1.0), (negs, 1.0), (ones, -1.0), (negs, -1.0)):
+        codes = np.full((R, K // 128, 32 if fmt == "pq2_0" else 26), byte, np.uint8)
+        W = TI.assemble_pq2(codes, sc) if fmt == "pq2_0" else TI.assemble_ptq1(codes, sc)
+        x = np.full((T, K), 127.0 * sign, np.float32)
+        check_integer_case(tq, orc, fmt, W, x, f"{fmt} extreme byte={byte} sign={sign}")
+        n += 1
+    zero = 0x55 if fmt == "pq2_0" else 0x80  # every weight 0 (code 1 / trits 1: 128 * 3^j = 128 mod 256)
+    codes = np.full((R, K // 128, 32 if fmt == "pq2_0" else 26), zero, np.uint8)
+    W = TI.assemble_pq2(codes, sc) if fmt == "pq2_0" else TI.assemble_ptq1(codes, sc)
+    w, _, _ = orc.decode(fmt, W)
+    assert not w.any()
+    check_integer_case(tq, orc, fmt, W, integer_activations(g, T, K), f"{fmt} zero weights")
+    say(f"integer grid {fmt}: {n + 1} cases")
+
+
 def test_one_hot_probes(tq, orc):
     """A single non-zero weight times a one-hot activation locates every
     (row, column) mapping of the repacked layout, for both formats."""
