@@ -21,7 +21,8 @@
 //     neither the stores nor the operand reads (16 tokens, one piece) collide
 //     in LDS banks; one barrier per superchunk.  The tokens' d_x for every
 //     superchunk are copied into LDS once, before the loop.
-//   * Codes, scales and activations are fetched D superchunks ahead into
+//   * Codes, scales and activations are fetched D superchunks ahead (4 for
+//     16-token blocks, 2 for 32-token blocks) into
 //     register rings with literal indices.  A prologue fills the ring and the
 //     main loop runs only while every fetch is real, so its body has no
 //     branch and the compiler's wait counts stay exact (no drain per pass);
@@ -44,7 +45,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Native vector types (not HIP's uint4 struct) keep copies in registers.
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kDepth = 4;
+// Register-ring depth in superchunks: measured on 17408 x 5120, 4 is best for
+// 16-token blocks (4 and 16 tokens; 2: 15.7 us at 4 tokens vs 12.4) and 2 for
+// 32-token blocks (64 tokens: 23.9 us vs 24.4); deeper rings are slower.
+template <int NT>
+constexpr int kDepth = NT == 1 ? 4 : 2;
 
 // LDS of the d_x copy: 16 * NT tokens x nsc superchunks of fp32, at most
 // 32 KiB (rows of up to 65536 columns with 32-token blocks)
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
   constexpr int NTOK = 16 * NT;
   constexpr int BPIECES = NTOK * 16;  // 16-byte activation pieces per superchunk
   constexpr int BPT = BPIECES / 256;  // per thread
-  constexpr int D = kDepth;
+  constexpr int D = kDepth<NT>;
   __shared__ v4u lds_b[2][BPIECES];
   extern __shared__ float lds_x[];  // d_x of the block's tokens, [superchunk][token]
   const int tid = threadIdx.x;
@@ -217,7 +222,8 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     TQ_FETCH(J, j + D)                                                                  \
   }
 
-  TQ_FETCH(0, 0) TQ_FETCH(1, 1) TQ_FETCH(2, 2) TQ_FETCH(3, 3)
+  TQ_FETCH(0, 0) TQ_FETCH(1, 1)
+  if constexpr (D > 2) { TQ_FETCH(2, 2) TQ_FETCH(3, 3) }
   if (!IDOTS) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) lds_x[min(tid + 256 * k, nx - 1)] = xr[k];
@@ -225,10 +231,12 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
   }
   int base = 0;
   for (; base + 2 * D <= nsc; base += D) {
-    TQ_STEP(0, true) TQ_STEP(1, true) TQ_STEP(2, true) TQ_STEP(3, true)
+    TQ_STEP(0, true) TQ_STEP(1, true)
+    if constexpr (D > 2) { TQ_STEP(2, true) TQ_STEP(3, true) }
   }
   for (; base < nsc; base += D) {
-    TQ_STEP(0, j < nsc) TQ_STEP(1, j < nsc) TQ_STEP(2, j < nsc) TQ_STEP(3, j < nsc)
+    TQ_STEP(0, j < nsc) TQ_STEP(1, j < nsc)
+    if constexpr (D > 2) { TQ_STEP(2, j < nsc) TQ_STEP(3, j < nsc) }
   }
 #undef TQ_STEP
 #undef TQ_FETCH
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     }
   }
 }
-static_assert(kDepth == 4, "the pass in gemm_pq2_kernel is written out for four steps");
+static_assert(kDepth<1> == 4 && kDepth<2> == 2, "the passes in gemm_pq2_kernel are written out for two or four steps");
 
 template <int NT>
 hipError_t launch_gemm_nt(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
