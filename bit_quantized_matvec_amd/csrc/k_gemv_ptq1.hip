@@ -38,9 +38,9 @@
 //     sum, so every launch shape gives the same bits;
 //   * one token: up to 8 waves per workgroup, one superblock each where the
 //     columns allow;
-//   * a prompt of several tokens runs NT tokens per workgroup (NT = 1, 2, 4
-//     or 8): each code dword is decoded once and its trits meet the NT
-//     tokens' tables, whose entries are interleaved by token.
+//   * a prompt of several tokens runs NT tokens per workgroup (NT = 1, 2 or
+//     4): each code dword is decoded once and its trits meet the NT tokens'
+//     tables, whose entries are interleaved by token.
 #include "kernels.h"
 
 namespace tq {
@@ -49,7 +49,7 @@ namespace {
 constexpr int kMaxWaves = 8;   // the kernel's limit
 constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock and token
 constexpr int kTasks = 48 + 8;                  // table-building tasks per superblock and token
-constexpr int kMaxTokBlock = 8;                 // tokens per workgroup
+constexpr int kMaxTokBlock = 4;                 // tokens per workgroup
 constexpr size_t kLdsBudget = 80 * 1024;        // two workgroups per compute unit
 
 // Dynamic LDS of a workgroup: the tables of scw superblocks for nt tokens.
@@ -459,11 +459,15 @@ hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, c
 }
 
 int ptq1_token_block(const Dims& dm, int64_t tokens) {
-  // the smallest power of two covering the tokens, at most 8, and no more
-  // than the LDS budget holds
+  // Blocks of 2 tokens up to 8 tokens, of 4 beyond, as far as the LDS budget
+  // allows.  Measured on 17408 x 5120 (blocks of 1 / 2 / 4 / 8): 4 tokens
+  // 29.0 / 20.9 / 21.9 / 47.9 us, 8 tokens 51.0 / 31.8 / 31.8 / 45.8 us,
+  // 64 tokens 362 / 189 / 177 / 200 us: one decode serves more tokens, but
+  // bigger tables cost occupancy, and two tokens take summation by parts.
   const GemvPlan p = plan_gemv_ptq1(dm, false);
+  const int want = tokens <= 8 ? 2 : kMaxTokBlock;
   int nt = 1;
-  while (nt < kMaxTokBlock && nt < tokens && ptq1_lds_bytes(p.scw, 2 * nt) <= kLdsBudget) nt *= 2;
+  while (nt < want && ptq1_lds_bytes(p.scw, 2 * nt) <= kLdsBudget) nt *= 2;
   return nt;
 }
 
@@ -482,8 +486,7 @@ hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, co
   switch (nt) {
     case 1: launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
     case 2: launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
-    case 4: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
-    default: launch_ptq1_nt<8>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
+    default: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
   }
   return hipGetLastError();
 }

@@ -176,7 +176,7 @@ int tq_gemv_f32_batch(int fmt, int n, const void *const *w, const int64_t *rows,
  * bit-identical to tq_gemv of token t without a workspace, for both formats,
  * so a batch of a few tokens gives exactly the outputs of one product per
  * token.  pq2_0 runs on int8 matrix cores; ptq1_0 decodes each base-3 byte
- * once per block of up to 8 tokens and takes the dot products on the vector
+ * once per block of up to 4 tokens and takes the dot products on the vector
  * units. */
 int tq_gemm(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q, const float *d,
             const int16_t *bsums, float *y, void *workspace, void *stream);

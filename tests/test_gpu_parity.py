@@ -310,7 +310,7 @@ def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
     pair's inner sum once and sum the superchunks in the same runs and run
     order; the column counts give runs of 1, 2, 2, 4 and 5 superchunks with
     ragged last runs.  ptq1_0: every token of a block takes the one-token
-    kernel's steps (blocks of 1, 2, 4 or 8 tokens, the last one padded).
+    kernel's steps (blocks of 1, 2 or 4 tokens, the last one padded).
     A workspace changes nothing (twice in a row, arrival counters at zero).
     17408x5120 is the prefill shape."""
     import torch
