@@ -28,13 +28,16 @@
 //     arrive sums the slices in slice order, writes y and resets the counter.
 //     The result is therefore deterministic, and no memset is needed between
 //     calls (safe inside a captured graph).
+#include <algorithm>
+
 #include "kernels.h"
 #include "q8k_block.h"
 
 namespace tq {
 namespace {
 
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = 16;  // the kernel's limit
+constexpr int kPlanWaves = 4;  // what the plan uses
 constexpr size_t kMaxStageBytes = 32 * 1024;  // LDS for one slice's staged activations
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -306,22 +309,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_batch_kernel(GemvBatc
 
 GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace) {
   // Measured on MI355X: with 384 or more row tiles one workgroup per tile is
-  // fastest (the extra workgroups of a split only add reduction work); with
-  // fewer tiles, splitting the columns until there are ~384 workgroups (each
-  // keeping at least 4 superchunks) fills the chip.  Up to 4 waves per
-  // workgroup, each with a run of superchunks.
+  // fastest (the extra workgroups of a split only add reduction work).  With
+  // fewer tiles, the columns are split into the fewest slices that keep each
+  // of 4 waves to a run of at most 3 superchunks and give at least 224
+  // workgroups, keeping at least 4 superchunks per slice (a split of a tiny
+  // row only adds the reduction: 256 x 1024 takes 2.9 us unsplit, 4.2 split).  Fused kernel, best
+  // split of a sweep vs this rule: 5120 x 6144 3 slices 5.97 us (rule: same;
+  // the earlier ~384-workgroup rule: 7.5 us), 7168 x 5120 2 slices 6.79 us
+  // (same; 7.25), 5120 x 17408 6 slices 10.42 us (same; 10.71), 17408 x 5120
+  // 3 slices 10.09 us (rule 2 slices: 10.65).
   GemvPlan p;
   const int nsc = (int)dm.nsc;
   int slices = 1;
   if (have_workspace && dm.ntiles < 384) {
-    slices = (int)((384 + dm.ntiles - 1) / dm.ntiles);
-    slices = slices < kMaxSlices ? slices : kMaxSlices;
-    const int most = nsc / 4 > 1 ? nsc / 4 : 1;
-    slices = slices < most ? slices : most;
+    const int most_slices = std::min(kMaxSlices, std::max(1, nsc / 4));
+    while (slices < most_slices && ((nsc + slices - 1) / slices > kPlanWaves * 3 || dm.ntiles * slices < 224)) ++slices;
   }
   p.scw = (nsc + slices - 1) / slices;
   p.slices = (nsc + p.scw - 1) / p.scw;
-  const int waves = p.scw < 4 ? p.scw : 4;
+  const int waves = p.scw < kPlanWaves ? p.scw : kPlanWaves;
   p.spw = (p.scw + waves - 1) / waves;
   p.waves = (p.scw + p.spw - 1) / p.spw;
   return p;

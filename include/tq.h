@@ -143,7 +143,9 @@ int tq_gemv(int fmt, const void *w, int64_t rows, int64_t cols, const int8_t *q,
  * workgroup's column slice must fit on chip (at most 126 blocks of 256, i.e.
  * 32256 columns): with n = cols / 256 and tiles = ceil(rows / 64), a slice is
  * ceil(n / s) blocks, s = 1 without a workspace or when tiles >= 384, else
- * s = min(16, ceil(384 / tiles), max(1, n / 4)).  Shapes beyond that, and
+ * s = the smallest value from 1 up to min(16, max(1, n / 4)) with
+ * ceil(n / s) <= 12 and tiles * s >= 224 (that cap if none).  Shapes beyond
+ * that, and
  * ptq1_0, return TQ_ERR_UNSUPPORTED (checked before the pointers) and touch
  * nothing. */
 int tq_gemv_f32(int fmt, const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *workspace,

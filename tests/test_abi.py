@@ -105,7 +105,11 @@ def test_validation_errors_touch_nothing(tq):
 def _fused_fits(rows, cols, ws):
     """The on-chip rule of tq_gemv_f32 as its declaration states it."""
     n, tiles = cols // 256, -(-rows // 64)
-    s = 1 if (not ws or tiles >= 384) else min(16, -(-384 // tiles), max(1, n // 4))
+    s = 1
+    if ws and tiles < 384:
+        most = min(16, max(1, n // 4))
+        while s < most and (-(-n // s) > 12 or tiles * s < 224):
+            s += 1
     return -(-n // s) <= 126
 
 
