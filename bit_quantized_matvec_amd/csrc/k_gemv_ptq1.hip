@@ -9,9 +9,9 @@
 //   * one lane = one row, a workgroup = a 64-row tile, waves split the
 //     8-group superblocks; 13 fully coalesced dwordx4 loads per row and
 //     superblock (1.75 bits per weight, bytes only reordered by the repack);
-//   * the four bytes of a code dword are split into two pairs of 16-bit lanes
-//     (bytes 0, 2 and bytes 1, 3), so one 32-bit multiply-by-3 advances two
-//     bytes at once without carries between them, and one v_perm_b32 gathers
+//   * the four bytes of a code dword are spread over the four 16-bit lanes of
+//     a 64-bit register, so one 64-bit shift-and-add (x + 2x) advances all
+//     four at once without carries between them, and one v_perm_b32 gathers
 //     the four high bytes into a dword = one dot4 operand.  Without masking
 //     between the multiplications the high byte after j + 1 of them is
 //     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1): with one or
@@ -57,25 +57,39 @@ constexpr size_t kLdsBudget = 80 * 1024;        // two workgroups per compute un
 // fp64 sums [token][lane] (512 bytes per token, within the 1792 of the table).
 size_t ptq1_lds_bytes(int scw, int nt) { return (size_t)nt * scw * kTableDwords * sizeof(uint32_t); }
 
+// LDS-typed pointers, so that an address passed through an asm statement
+// still yields LDS reads.
+typedef __attribute__((address_space(3))) const uint32_t* lds_cptr;
+typedef unsigned lds_v4 __attribute__((ext_vector_type(4)));
+typedef unsigned lds_v2 __attribute__((ext_vector_type(2)));
+
 // `L` consecutive dwords of LDS from a 16-byte aligned address, in as few
 // reads as the alignment allows.
 template <int L>
-__device__ __forceinline__ void lds_run(const uint32_t* p, uint32_t* v) {
-  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void lds_run(lds_cptr p, uint32_t* v) {
+  typedef __attribute__((address_space(3))) const lds_v4* P4;
+  typedef __attribute__((address_space(3))) const lds_v2* P2;
+  const P4 p4 = (P4)p;
 #pragma unroll
   for (int i = 0; i < L / 4; ++i) {
-    const uint4 t = p4[i];
+    const lds_v4 t = p4[i];
     v[4 * i] = t.x;
     v[4 * i + 1] = t.y;
     v[4 * i + 2] = t.z;
     v[4 * i + 3] = t.w;
   }
   if constexpr (L % 4 >= 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p + L / 4 * 4);
+    const lds_v2 t = *(P2)(p + L / 4 * 4);
     v[L / 4 * 4] = t.x;
     v[L / 4 * 4 + 1] = t.y;
   }
   if constexpr (L % 2 == 1) v[L - 1] = p[L - 1];
+}
+
+__device__ __forceinline__ uint64_t times3(uint64_t x) {
+  uint64_t r;
+  asm("v_lshl_add_u64 %0, %1, 1, %1" : "=v"(r) : "v"(x));
+  return r;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -201,21 +215,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = 0.0;
     // Loads 0..11 hold the 48 full dwords (3 loads per group pair), load 12
-    // the four leftover dwords.  One group pair is decoded per iteration,
-    // with the next pair's three loads already in flight.
+    // the four leftover dwords.  All 13 and the scales are requested at once,
+    // in the order they are used; group pair gp waits for its own three.
     const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
-    const uint4 left = cp[12 * 64];
+    uint4 cw[13];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) cw[k] = cp[k * 64];
+    cw[12] = cp[12 * 64];
     const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
+#pragma unroll
+    for (int k = 3; k < 12; ++k) cw[k] = cp[k * 64];
+    const uint4 left = cw[12];
     const uint32_t* tb = table + (size_t)(sb - wg0) * kTableDwords * NT;
-    uint4 cur[3] = {cp[0], cp[64], cp[128]};
-#pragma unroll 1
+#pragma unroll
     for (int gp = 0; gp < 4; ++gp) {
-      uint4 nxt[3] = {cur[0], cur[1], cur[2]};
-      if (gp < 3) {
-        nxt[0] = cp[(3 * gp + 3) * 64];
-        nxt[1] = cp[(3 * gp + 4) * 64];
-        nxt[2] = cp[(3 * gp + 5) * 64];
-      }
+      const uint4* cur = cw + 3 * gp;
       const uint32_t dws[13] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z,
                                 cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
                                 gp == 0 ? left.x : gp == 1 ? left.y : gp == 2 ? left.z : left.w};
@@ -226,44 +240,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       for (int n = 0; n < NT; ++n) ia[n] = ib[n] = ja[n] = jb[n] = 0;
       // Table entries of dword m: 5 levels (10 level-halves for the leftover
       // dword m = 12) x NT tokens, entry (level, token) at te[level * NT + token].
-      // With one token all reads of a dword are issued together and the
-      // compiler schedules them; with more, the reads of dword m + 1 are
-      // issued before the products of dword m and no earlier (opaque offsets
-      // and accumulators order them), so that two dwords' entries at most
-      // are held in registers.
+      // The reads of dword m + 1 are issued before the products of dword m
+      // and no earlier, so that two dwords' entries at most are held in
+      // registers: the table's base address passes through an empty asm
+      // statement once per dword, which keeps the compiler from merging or
+      // hoisting reads across dwords (the constant offsets still fold into
+      // the read instructions).
       constexpr int kLev = 5 * NT, kLeft = 10 * NT;
-      constexpr bool kAll = NT == 1;
       // With one or two tokens summation by parts (below) saves VALU; with
       // more, its extra dot per level and token outweighs the masks it saves.
       constexpr bool kParts = NT <= 2;
       auto te_off = [&](int m) { return m < 12 ? (12 * gp + m) * 8 * NT : (48 * 8 + gp * 16) * NT; };
       uint32_t tnext[kLeft];
-      if constexpr (!kAll) {
-        int off = te_off(0);
-        asm volatile("" : "+v"(off));
-        lds_run<kLev>(tb + off, tnext);
-      }
+      lds_cptr tbl = (lds_cptr)tb;
+      asm volatile("" : "+v"(tbl));
+      lds_run<kLev>(tbl + te_off(0), tnext);
 #pragma unroll
       for (int m = 0; m < 13; ++m) {
         const uint32_t d = dws[m];
         uint32_t tv[kLeft];
-        if constexpr (kAll) {
-          const uint32_t* te = tb + te_off(m);
-          if (m < 12) lds_run<kLev>(te, tv);
-          else lds_run<kLeft>(te, tv);
-        } else {
 #pragma unroll
-          for (int i = 0; i < kLeft; ++i) tv[i] = tnext[i];
-          if (m + 1 < 13) {
-            int off = te_off(m + 1);
-            asm volatile("" : "+v"(off));
-            if (m + 1 < 12) lds_run<kLev>(tb + off, tnext);
-            else lds_run<kLeft>(tb + off, tnext);
-          }
+        for (int i = 0; i < kLeft; ++i) tv[i] = tnext[i];
+        if (m + 1 < 13) {
+          asm volatile("" : "+v"(tbl));
+          if (m + 1 < 12) lds_run<kLev>(tbl + te_off(m + 1), tnext);
+          else lds_run<kLeft>(tbl + te_off(m + 1), tnext);
         }
-        // bytes 0, 2 and bytes 1, 3 of the code dword in 16-bit lanes
-        uint32_t e = __builtin_amdgcn_perm(0u, d, 0x0C020C00u);
-        uint32_t o = __builtin_amdgcn_perm(0u, d, 0x0C030C01u);
+        // the four bytes of the code dword in the four 16-bit lanes of E
+        // (bytes 0, 1 in the low dword, 2, 3 in the high one); after each
+        // multiplication by 3 the high bytes of the lanes, bytes 1, 3 of each
+        // dword, are gathered in byte order by one v_perm_b32
+        uint64_t E = ((uint64_t)__builtin_amdgcn_perm(0u, d, 0x0C030C02u) << 32) |
+                     (uint64_t)__builtin_amdgcn_perm(0u, d, 0x0C010C00u);
+        auto high_bytes = [](uint64_t v) { return __builtin_amdgcn_perm((uint32_t)(v >> 32), (uint32_t)v, 0x07050301u); };
         if (kParts && m < 12) {
           // Summation by parts.  With h_j = floor(b 3^(j+1) / 256), the high
           // byte of the 16-bit lane after j + 1 multiplications by 3 (b 3^5
@@ -274,9 +283,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
           uint32_t hprev = 0;
 #pragma unroll
           for (int j = 0; j < 5; ++j) {
-            e *= 3u;
-            o *= 3u;
-            const uint32_t hj = __builtin_amdgcn_perm(o, e, 0x07030501u);  // bytes 1, 3 of e and of o
+            E = times3(E);
+            const uint32_t hj = high_bytes(E);
             if (j < 4) {
 #pragma unroll
               for (int n = 0; n < NT; ++n) {
@@ -302,9 +310,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
           // keeps v_(j+1) = 3v mod 256 (the leftover dword pairs two groups)
 #pragma unroll
           for (int j = 0; j < 5; ++j) {
-            e *= 3u;
-            o *= 3u;
-            const int t = (int)__builtin_amdgcn_perm(o, e, 0x07030501u);
+            E = times3(E);
+            const int t = (int)high_bytes(E);
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
               if (m < 6) {
@@ -316,16 +323,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
                 ib[n] = __builtin_amdgcn_sdot4(t, (int)tv[(2 * j + 1) * NT + n], ib[n], false);
               }
             }
-            e &= 0x00FF00FFu;
-            o &= 0x00FF00FFu;
+            E &= 0x00FF00FF00FF00FFull;
           }
         }
-        if constexpr (!kAll) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
-            if constexpr (kParts) asm volatile("" : "+v"(ja[n]), "+v"(jb[n]));
-          }
+        for (int n = 0; n < NT; ++n) {
+          asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
+          if constexpr (kParts) asm volatile("" : "+v"(ja[n]), "+v"(jb[n]));
         }
       }
       const uint32_t s2 = gp == 0 ? sc8.x : gp == 1 ? sc8.y : gp == 2 ? sc8.z : sc8.w;
@@ -347,9 +351,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
           }
         }
       }
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
-      cur[2] = nxt[2];
     }
     if (!IDOTS) {
       // this wave has read the last of the superblock's table (LDS operations
