@@ -14,10 +14,10 @@
 //     four at once without carries between them, and one v_perm_b32 gathers
 //     the four high bytes into a dword = one dot4 operand.  Without masking
 //     between the multiplications the high byte after j + 1 of them is
-//     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1): with one or
-//     two tokens, summation by parts turns the trit dot into h dots against
-//     the activations and their next-trit neighbours (no masks); with more
-//     tokens each trit is masked out and dotted once per token;
+//     h_j = floor(b 3^(j+1) / 256), and trit j is h_j - 3 h_(j-1):
+//     summation by parts turns the trit dot into h dots against the
+//     activations and their next-trit neighbours (no masks); the leftover
+//     dword, whose halves belong to two groups, is masked trit by trit;
 //   * the trits are w + 1, so I = dot(t, q) - sum(q), the group sum coming
 //     from the q8_K partial sums (page 1, "the trick with 4 and 16": sum(y)
 //     over 128 values is one add over 8 partial sums);
@@ -31,16 +31,20 @@
 //     q and its d_x, so the products read nothing but LDS (scalar loads in
 //     the loop would make every LDS wait a full one: they return out of
 //     order);
-//   * the fp64 sum has one fixed order whatever the launch: the terms of a
-//     superblock's 8 groups are added in group order from zero, and the
-//     superblock sums in superblock order.  Waves, column slices (with a
-//     workspace) and token blocks only change who computes which superblock
-//     sum, so every launch shape gives the same bits;
+//   * the fp64 sum has one fixed order whatever the launch: per group pair
+//     (groups 2p, 2p + 1 share one q8_K block) inner = d_w(2p+1) I1 +
+//     d_w(2p) I0 and acc = d_x inner + acc, each with one rounding, acc from
+//     zero per superblock in pair order, and the superblock sums in
+//     superblock order.  Waves, column slices (with a workspace) and token
+//     blocks only change who computes which superblock sum, so every launch
+//     shape -- and the MFMA prompt product, which uses the same sequence --
+//     gives the same bits;
 //   * one token: up to 8 waves per workgroup, one superblock each where the
 //     columns allow;
-//   * a prompt of several tokens runs NT tokens per workgroup (NT = 1, 2 or
-//     4): each code dword is decoded once and its trits meet the NT tokens'
-//     tables, whose entries are interleaved by token.
+//   * a prompt of up to 7 tokens runs NT tokens per workgroup (NT = 1 or
+//     2): each code dword is decoded once and its trits meet the NT tokens'
+//     tables, whose entries are interleaved by token.  Longer prompts go to
+//     the MFMA kernel of k_gemm_ptq1.hip.
 #include "kernels.h"
 
 namespace tq {
@@ -49,7 +53,8 @@ namespace {
 constexpr int kMaxWaves = 8;   // the kernel's limit
 constexpr int kTableDwords = 48 * 8 + 4 * 16;  // per superblock and token
 constexpr int kTasks = 48 + 8;                  // table-building tasks per superblock and token
-constexpr int kMaxTokBlock = 4;                 // tokens per workgroup
+constexpr int kMaxTokBlock = 2;                 // tokens per workgroup
+constexpr int kMfmaMinTokens = 8;               // from here on prompts go to the MFMA kernel
 constexpr size_t kLdsBudget = 80 * 1024;        // two workgroups per compute unit
 
 // Dynamic LDS of a workgroup: the tables of scw superblocks for nt tokens.
@@ -247,9 +252,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
       // hoisting reads across dwords (the constant offsets still fold into
       // the read instructions).
       constexpr int kLev = 5 * NT, kLeft = 10 * NT;
-      // With one or two tokens summation by parts (below) saves VALU; with
-      // more, its extra dot per level and token outweighs the masks it saves.
-      constexpr bool kParts = NT <= 2;
       auto te_off = [&](int m) { return m < 12 ? (12 * gp + m) * 8 * NT : (48 * 8 + gp * 16) * NT; };
       uint32_t tnext[kLeft];
       lds_cptr tbl = (lds_cptr)tb;
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
         uint64_t E = ((uint64_t)__builtin_amdgcn_perm(0u, d, 0x0C030C02u) << 32) |
                      (uint64_t)__builtin_amdgcn_perm(0u, d, 0x0C010C00u);
         auto high_bytes = [](uint64_t v) { return __builtin_amdgcn_perm((uint32_t)(v >> 32), (uint32_t)v, 0x07050301u); };
-        if (kParts && m < 12) {
+        if (m < 12) {
           // Summation by parts.  With h_j = floor(b 3^(j+1) / 256), the high
           // byte of the 16-bit lane after j + 1 multiplications by 3 (b 3^5
           // < 2^16, so nothing spills into the next lane), trit j is
@@ -329,25 +331,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           asm volatile("" : "+v"(ia[n]), "+v"(ib[n]));
-          if constexpr (kParts) asm volatile("" : "+v"(ja[n]), "+v"(jb[n]));
+          asm volatile("" : "+v"(ja[n]), "+v"(jb[n]));
         }
       }
       const uint32_t s2 = gp == 0 ? sc8.x : gp == 1 ? sc8.y : gp == 2 ? sc8.z : sc8.w;
+      const int g0 = sb * 8 + 2 * gp;
+      if (g0 < G) {  // G is even: both groups of the pair exist
+        // the groups' sums of q, then their d_x (the same q8_K block)
+        const uint32_t* gs0 = tb + (8 * 6 * (2 * gp) + 6) * NT;
+        const uint32_t* gs1 = tb + (8 * 6 * (2 * gp + 1) + 6) * NT;
+        const double dw0 = (double)half_bits_to_float(s2 & 0xffffu);
+        const double dw1 = (double)half_bits_to_float(s2 >> 16);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = sb * 8 + 2 * gp + h;
-        if (g < G) {
-          const double dw = (double)half_bits_to_float(h ? (s2 >> 16) : (s2 & 0xffffu));
-          const uint32_t* gs = tb + (8 * 6 * (2 * gp + h) + 6) * NT;  // the group's sum of q, then d_x
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            const int qsum = (int)gs[n];
-            const int I = (h ? ib[n] - 3 * jb[n] : ia[n] - 3 * ja[n]) - qsum;
-            if (IDOTS) {
-              if (row < rows && tok0 + n < tokens) idots[((size_t)(tok0 + n) * rows + row) * G + g] = I;
-            } else {
-              acc[n] += (dw * (double)__builtin_bit_cast(float, gs[NT + n])) * (double)I;
+        for (int n = 0; n < NT; ++n) {
+          const int I0 = ia[n] - 3 * ja[n] - (int)gs0[n];
+          const int I1 = ib[n] - 3 * jb[n] - (int)gs1[n];
+          if (IDOTS) {
+            if (row < rows && tok0 + n < tokens) {
+              const size_t o = ((size_t)(tok0 + n) * rows + row) * G + g0;
+              idots[o] = I0;
+              idots[o + 1] = I1;
             }
+          } else {
+            // inner = d_w1 I1 + d_w0 I0 (d_w0 I0 exact, one rounding), then
+            // acc = d_x inner + acc (one rounding)
+            const double inner = __builtin_fma(dw1, (double)I1, dw0 * (double)I0);
+            acc[n] = __builtin_fma((double)__builtin_bit_cast(float, gs0[NT + n]), inner, acc[n]);
           }
         }
       }
@@ -460,20 +469,21 @@ hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, c
 }
 
 int ptq1_token_block(const Dims& dm, int64_t tokens) {
-  // Blocks of 2 tokens up to 8 tokens, of 4 beyond, as far as the LDS budget
-  // allows.  Measured on 17408 x 5120 (blocks of 1 / 2 / 4 / 8): 4 tokens
-  // 29.0 / 20.9 / 21.9 / 47.9 us, 8 tokens 51.0 / 31.8 / 31.8 / 45.8 us,
-  // 64 tokens 362 / 189 / 177 / 200 us: one decode serves more tokens, but
-  // bigger tables cost occupancy, and two tokens take summation by parts.
+  // Blocks of 2 tokens where the LDS budget allows (measured on 17408 x 5120
+  // with blocks of 1 / 2 / 4: 4 tokens 29.0 / 20.9 / 21.9 us): one decode
+  // serves two tokens, and two tokens take summation by parts.
   const GemvPlan p = plan_gemv_ptq1(dm, false);
-  const int want = tokens <= 8 ? 2 : kMaxTokBlock;
   int nt = 1;
-  while (nt < want && ptq1_lds_bytes(p.scw, 2 * nt) <= kLdsBudget) nt *= 2;
+  while (nt < kMaxTokBlock && nt < tokens && ptq1_lds_bytes(p.scw, 2 * nt) <= kLdsBudget) nt *= 2;
   return nt;
 }
 
 hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                             const int16_t* bsums, float* y, int32_t* idots, hipStream_t s) {
+  // From 8 tokens on the MFMA kernel (measured on 17408 x 5120, vector
+  // units / MFMA: 4 tokens 20.2 / 28.3 us, 8 tokens 34.2 / 28.1, 16 tokens
+  // 48.6 / 28.4, 64 tokens 163 / 56.6); it sums in the same order.
+  if (tokens >= kMfmaMinTokens) return launch_gemm_ptq1_mfma(w, dm, tokens, q, dx, bsums, y, idots, s);
   // one workgroup per tile and token block, with the one-token plan's waves
   // (the summation order does not depend on the split)
   const GemvPlan p = plan_gemv_ptq1(dm, false);
@@ -484,11 +494,10 @@ hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, co
   const size_t lds = ptq1_lds_bytes(p.scw, nt);
   const bool io = idots != nullptr;
   const int T = (int)tokens;
-  switch (nt) {
-    case 1: launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
-    case 2: launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
-    default: launch_ptq1_nt<4>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T); break;
-  }
+  if (nt == 1)
+    launch_ptq1_nt<1>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T);
+  else
+    launch_ptq1_nt<2>(io, grid, block, lds, s, codes, scales, q, dx, bsums, y, idots, dm, p, nullptr, T);
   return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, c
 int ptq1_token_block(const Dims& dm, int64_t tokens);
 hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                             const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
+// The same on int8 MFMA: 32 tokens x 128 rows per workgroup.
+hipError_t launch_gemm_ptq1_mfma(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
+                                 const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
 // y[tokens][rows] or idots [tokens][rows][G].
 hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                            float* y, int32_t* idots, hipStream_t s);

@@ -177,9 +177,10 @@ int tq_gemv_f32_batch(int fmt, int n, const void *const *w, const int64_t *rows,
  * with more than one token it is not used.  With tokens > 1, y[t] is
  * bit-identical to tq_gemv of token t without a workspace, for both formats,
  * so a batch of a few tokens gives exactly the outputs of one product per
- * token.  pq2_0 runs on int8 matrix cores; ptq1_0 decodes each base-3 byte
- * once per block of up to 4 tokens and takes the dot products on the vector
- * units. */
+ * token.  pq2_0 runs on int8 matrix cores.  ptq1_0 with up to 7 tokens
+ * decodes each base-3 byte once per block of 2 tokens and takes the dot
+ * products on the vector units; from 8 tokens on it decodes once per 16
+ * tokens and runs on int8 matrix cores. */
 int tq_gemm(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q, const float *d,
             const int16_t *bsums, float *y, void *workspace, void *stream);
 
