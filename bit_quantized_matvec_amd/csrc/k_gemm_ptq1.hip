@@ -173,16 +173,13 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
         uint32_t w[5];
 #pragma unroll
         for (int k = 0; k < 5; ++k) w[k] = src[5 * c + k];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int by = 5 * b + j;  // byte of the 20
-            v |= byte(w[by >> 2], by & 3) << (8 * b);
-          }
-          e[j] = v;
-        }
+        // e[j] = bytes j, 5 + j, 10 + j, 15 + j of the 20: two byte permutes
+        // of two dwords each, merged
+        e[0] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0500u) | __builtin_amdgcn_perm(w[3], w[2], 0x07020C0Cu);
+        e[1] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0601u) | __builtin_amdgcn_perm(w[4], w[2], 0x04030C0Cu);
+        e[2] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0702u) | __builtin_amdgcn_perm(w[4], w[3], 0x05000C0Cu);
+        e[3] = __builtin_amdgcn_perm(w[2], w[0], 0x0C0C0403u) | __builtin_amdgcn_perm(w[4], w[3], 0x06010C0Cu);
+        e[4] = __builtin_amdgcn_perm(w[2], w[1], 0x0C0C0500u) | __builtin_amdgcn_perm(w[4], w[3], 0x07020C0Cu);
         lq = c & 3;
         u0 = c < 4 ? 0 : 5;
       } else {
