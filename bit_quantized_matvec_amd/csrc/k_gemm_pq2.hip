@@ -51,6 +51,9 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 template <int NT>
 constexpr int kDepth = NT == 1 ? 4 : 2;
 
+// Workgroups per token block of the balanced grid: one per compute unit.
+constexpr int kBalancedWgs = 256;
+
 // LDS of the d_x copy: 16 * NT tokens x nsc superchunks of fp32, at most
 // 32 KiB (rows of up to 65536 columns with 32-token blocks)
 constexpr size_t gemm_dx_bytes(int nsc, int nt) { return (size_t)nsc * 16 * nt * 4; }
@@ -74,26 +77,56 @@ __device__ __forceinline__ double hi_half(uint32_t p) {
 
 // Grid: ntb token blocks per tile, laid out so that the blocks of one tile
 // share blockIdx.x % 8: id = (grp * ntb + tb) * 8 + (tile % 8), grp = tile / 8.
-template <int NT, bool IDOTS>
-__global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ codes, const uint32_t* __restrict__ scales,
-                                                       const int8_t* __restrict__ q, const float* __restrict__ dx,
-                                                       float* __restrict__ y, int32_t* __restrict__ idots, int rows,
-                                                       int ntiles, int nsc, int tokens, int ntb, int spw) {
+//
+// BAL (a little over 256 tiles, where one workgroup per tile would leave
+// some compute units with two and most with one): 256 workgroups per token
+// block of 5 waves each, each taking 4 or 5 consecutive 16-row blocks (one
+// per wave; a fifth wave without a block only takes part in the barriers), evenly
+// over the XCDs.  Every wave still runs the whole row of superchunks, so the
+// sums are the same.
+template <int NT, bool IDOTS, bool BAL>
+__global__ __launch_bounds__(BAL ? 320 : 256) void gemm_pq2_kernel(const v4u* __restrict__ codes,
+                                                                  const uint32_t* __restrict__ scales,
+                                                                  const int8_t* __restrict__ q,
+                                                                  const float* __restrict__ dx, float* __restrict__ y,
+                                                                  int32_t* __restrict__ idots, int rows, int ntiles,
+                                                                  int nsc, int tokens, int ntb, int spw, int nwg) {
   constexpr int NTOK = 16 * NT;
   constexpr int BPIECES = NTOK * 16;  // 16-byte activation pieces per superchunk
-  constexpr int BPT = BPIECES / 256;  // per thread
+  constexpr int BPT = BPIECES / 256;  // per staging thread (the first 256)
   constexpr int D = kDepth<NT>;
   __shared__ v4u lds_b[2][BPIECES];
   extern __shared__ float lds_x[];  // d_x of the block's tokens, [superchunk][token]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int rb = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, qd = lane >> 4;
   const int id = blockIdx.x;
   const int grp = id / (8 * ntb), rem = id % (8 * ntb);
-  const int tile = grp * 8 + (rem % 8);
+  const int unit = grp * 8 + (rem % 8);
   const int tb = rem / 8;
-  if (tile >= ntiles) return;  // padding of the last group of 8 tiles (uniform)
+  if (unit >= (BAL ? nwg : ntiles)) return;  // padding of the last group of 8 (uniform)
+  int tile = unit, rb = wv;
+  bool active = true;  // this wave owns a 16-row block
+  if (BAL) {
+    // XCD x = unit % 8 (the dispatch order) gets blocks [x nblk / 8,
+    // (x + 1) nblk / 8), split over its nwg / 8 workgroups, so that every XCD
+    // and every compute unit gets the same share
+    const int nblk = 4 * ntiles, x = unit & 7, l = unit >> 3, nx = nwg >> 3;
+    const int x0 = x * nblk / 8, xn = (x + 1) * nblk / 8 - x0;
+    const int base = xn / nx, extra = xn - base * nx;  // the first `extra` workgroups take one more
+    const int b0 = x0 + base * l + min(l, extra), nb = base + (l < extra ? 1 : 0);
+    active = wv < nb;
+    const int b = b0 + min(wv, nb - 1);
+    tile = b >> 2;
+    rb = b & 3;
+  }
+  const bool stager = tid < 256;
+  if (BAL && !active && !stager) {
+    // a fifth wave without a block: only the per-superchunk barriers
+    for (int j = 0; j < nsc; ++j) __syncthreads();
+    return;
+  }
   const int tok0 = tb * NTOK;
   const int K = nsc * 256, G = 2 * nsc;
 
@@ -103,7 +136,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
   int b_dst[BPT];
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    const int slot = k * 256 + tid;
+    const int slot = k * 256 + (tid & 255);  // the fifth wave re-reads the first's pieces and stores none
     const int t = slot >> 4, p = slot & 15;
     b_src[k] = q + (size_t)min(tok0 + t, tokens - 1) * K + 16 * p;  // + sc * 256
     b_dst[k] = t * 16 + (p ^ (t & 15));
@@ -214,10 +247,14 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
     const int j = base + J;                                                             \
     if (LIVE) {                                                                         \
       const int buf = j & 1;                                                            \
-      _Pragma("unroll") for (int k = 0; k < BPT; ++k) lds_b[buf][b_dst[k]] = rbv[J][k]; \
+      if (stager) {                                                                     \
+        _Pragma("unroll") for (int k = 0; k < BPT; ++k) lds_b[buf][b_dst[k]] = rbv[J][k]; \
+      }                                                                                 \
       __syncthreads();                                                                  \
-      compute(buf, ra[J], rs[J], j);                                                    \
-      if (!IDOTS) fold_run(j);                                                          \
+      if (active) {                                                                     \
+        compute(buf, ra[J], rs[J], j);                                                  \
+        if (!IDOTS) fold_run(j);                                                        \
+      }                                                                                 \
     }                                                                                   \
     TQ_FETCH(J, j + D)                                                                  \
   }
@@ -241,7 +278,7 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
 #undef TQ_STEP
 #undef TQ_FETCH
 
-  if (IDOTS) return;
+  if (IDOTS || !active) return;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int row = tile * 64 + 16 * rb + 4 * qd + v;
@@ -254,24 +291,35 @@ __global__ __launch_bounds__(256) void gemm_pq2_kernel(const v4u* __restrict__ c
 }
 static_assert(kDepth<1> == 4 && kDepth<2> == 2, "the passes in gemm_pq2_kernel are written out for two or four steps");
 
-template <int NT>
-hipError_t launch_gemm_nt(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
-                          int32_t* idots, hipStream_t s) {
+template <int NT, bool BAL>
+hipError_t launch_gemm_ntb(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
+                           int32_t* idots, hipStream_t s) {
   const int nsc = (int)dm.nsc;
   const int ntb = (int)((tokens + 16 * NT - 1) / (16 * NT));
-  const int64_t groups = (dm.ntiles + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * ntb)), block(256);
+  const int nwg = BAL ? kBalancedWgs : (int)dm.ntiles;
+  const int64_t groups = (nwg + 7) / 8;
+  const dim3 grid((unsigned)(groups * 8 * ntb)), block(BAL ? 320 : 256);
   const v4u* codes = reinterpret_cast<const v4u*>(w);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
   // the run length of the matrix-vector product without a workspace
   const int spw = plan_gemv_pq2(dm, false).spw;
   if (idots)
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, true>), grid, block, 0, s, codes, scales, q, dx, y, idots, (int)dm.rows,
-                       (int)dm.ntiles, nsc, (int)tokens, ntb, spw);
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, true, BAL>), grid, block, 0, s, codes, scales, q, dx, y, idots,
+                       (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb, spw, nwg);
   else
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, false>), grid, block, (unsigned)gemm_dx_bytes(nsc, NT), s, codes, scales, q,
-                       dx, y, idots, (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb, spw);
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, false, BAL>), grid, block, (unsigned)gemm_dx_bytes(nsc, NT), s, codes,
+                       scales, q, dx, y, idots, (int)dm.rows, (int)dm.ntiles, nsc, (int)tokens, ntb, spw, nwg);
   return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_gemm_nt(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
+                          int32_t* idots, hipStream_t s) {
+  // a little over 256 tiles: the balanced grid (4 or 5 row blocks per
+  // workgroup, 256 workgroups per token block)
+  if (dm.ntiles > kBalancedWgs && dm.ntiles * 4 <= kBalancedWgs * 5)
+    return launch_gemm_ntb<NT, true>(w, dm, tokens, q, dx, y, idots, s);
+  return launch_gemm_ntb<NT, false>(w, dm, tokens, q, dx, y, idots, s);
 }
 
 }  // namespace
