@@ -32,9 +32,10 @@
 //     order.  The matrix-vector product uses the same sequence, so every
 //     token's output is bit-identical to it.
 //   * Workgroup = 4 waves = one 64-row tile and 16 tokens (45 KiB of LDS:
-//     three workgroups per compute unit); the codes of the next group pair
-//     and the staging inputs of the next superblock are loaded while the
-//     current ones are used.
+//     three workgroups per compute unit); each lane loads exactly the code
+//     dwords it decodes (16 per superblock), and those and the staging
+//     inputs of the next superblock are loaded while the current ones are
+//     used.
 //   * Tokens past the end read a valid token (the last) and rows past the
 //     end have zero codes and scales; neither is stored.
 #include "kernels.h"
