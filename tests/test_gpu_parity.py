@@ -640,13 +640,23 @@ def test_gemm_ptq1_token_blocks(tq, orc, R, K, T):
 
 
 def test_max_columns(tq, orc):
+    """The column limits of the ABI (pq2_0 2^20, ptq1_0 32768) and a wide
+    pq2_0 case below it: one token, then a two-token prompt, without and with
+    a workspace (column slices)."""
     g = TI.rng(77, 11)
-    for fmt, K in (("pq2_0", 65536), ("ptq1_0", 32768)):
+    for fmt, K in (("pq2_0", 65536), ("pq2_0", 1 << 20), ("ptq1_0", 32768)):
         say("max cols", fmt, K)
-        W = TI.pq2_matrix(g, 3, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, 3, K)
-        x = TI.activations(g, 1, K)
-        _, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
+        R = 3
+        W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
+        x = TI.activations(g, 2, K)
         qo, do, _ = orc.quantize_q8k(x)
-        assert np.array_equal(I, orc.group_dots(fmt, W, qo))
         yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
-        assert_close_rows(y, yo, mag, what=f"max cols {fmt}")
+        Wd, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x[:1])
+        assert np.array_equal(I, orc.group_dots(fmt, W, qo[:1]))
+        assert_close_rows(y, yo[:1], mag[:1], what=f"max cols {fmt} {K}")
+        ws = tq.workspace(fmt, R, K)
+        qd, dd, bsd = tq.quantize_q8k(dev(x))
+        yw = host(tq.gemv(fmt, Wd, R, K, qd[1], dd[1], bsd[1], ws=ws))
+        assert_close_rows(yw.reshape(1, R), yo[1:], mag[1:], what=f"max cols {fmt} {K} workspace")
+        y2 = host(tq.gemm(fmt, Wd, R, K, qd, dd, bsd))
+        assert_close_rows(y2, yo, mag, what=f"max cols {fmt} {K} prompt")
