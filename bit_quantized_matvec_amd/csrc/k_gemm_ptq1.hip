@@ -38,6 +38,8 @@
 //     used.
 //   * Tokens past the end read a valid token (the last) and rows past the
 //     end have zero codes and scales; neither is stored.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace tq {
@@ -305,14 +307,27 @@ hipError_t launch_gemm_ptq1_mfma(const uint8_t* w, const Dims& dm, int64_t token
                                  const int16_t* bsums, float* y, int32_t* idots, hipStream_t s) {
   const v4u* codes = reinterpret_cast<const v4u*>(w);
   const v4u* scales = reinterpret_cast<const v4u*>(w + ptq1_code_bytes(dm));
-  const dim3 grid((unsigned)dm.ntiles, (unsigned)((tokens + kTok - 1) / kTok)), block(256);
-  if (idots)
-    hipLaunchKernelGGL((gemm_ptq1_kernel<true>), grid, block, 0, s, codes, scales, q, dx, bsums, y, idots,
-                       (int)dm.rows, (int)dm.G, (int)dm.G8, (int)tokens);
-  else
-    hipLaunchKernelGGL((gemm_ptq1_kernel<false>), grid, block, 0, s, codes, scales, q, dx, bsums, y, idots,
-                       (int)dm.rows, (int)dm.G, (int)dm.G8, (int)tokens);
-  return hipGetLastError();
+  // The token blocks go in grid.y, whose extent is kept below 2^16: longer
+  // prompts are launched in chunks of 2^15 token blocks, each with its
+  // tokens' activations and outputs.
+  constexpr int64_t kChunk = int64_t(kTok) << 15;
+  const int64_t K = dm.cols, R = dm.rows, G = dm.G;
+  for (int64_t t0 = 0; t0 < tokens; t0 += kChunk) {
+    const int64_t nt = std::min(kChunk, tokens - t0);
+    const int8_t* qc = q + t0 * K;
+    const float* dxc = dx ? dx + t0 * (K / 256) : nullptr;
+    const int16_t* bc = bsums + t0 * (K / 16);
+    const dim3 grid((unsigned)dm.ntiles, (unsigned)((nt + kTok - 1) / kTok)), block(256);
+    if (idots)
+      hipLaunchKernelGGL((gemm_ptq1_kernel<true>), grid, block, 0, s, codes, scales, qc, dxc, bc, nullptr,
+                         idots + t0 * R * G, (int)R, (int)G, (int)dm.G8, (int)nt);
+    else
+      hipLaunchKernelGGL((gemm_ptq1_kernel<false>), grid, block, 0, s, codes, scales, qc, dxc, bc, y + t0 * R,
+                         nullptr, (int)R, (int)G, (int)dm.G8, (int)nt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tq

@@ -660,3 +660,19 @@ def test_max_columns(tq, orc):
         assert_close_rows(yw.reshape(1, R), yo[1:], mag[1:], what=f"max cols {fmt} {K} workspace")
         y2 = host(tq.gemm(fmt, Wd, R, K, qd, dd, bsd))
         assert_close_rows(y2, yo, mag, what=f"max cols {fmt} {K} prompt")
+
+
+def test_gemm_ptq1_token_chunks(tq, orc):
+    """A ptq1_0 prompt long enough that the MFMA kernel is launched in two
+    chunks of token blocks (2^19 tokens, then 17 more: a ragged last block)."""
+    R, K, T = 3, 256, (1 << 19) + 17
+    g = TI.rng(77, 19, R, K)
+    W = TI.ptq1_matrix(g, R, K)
+    x = TI.activations(g, T, K)
+    say("gemm ptq1 token chunks", R, K, T)
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, "ptq1_0", W, x)
+    qo, do, _ = orc.quantize_q8k(x)
+    assert np.array_equal(q, qo)
+    assert np.array_equal(I, orc.group_dots("ptq1_0", W, qo))
+    yo, mag = orc.matmul("ptq1_0", W, qo, do, with_mag=True)
+    assert_close_rows(y, yo, mag, what=f"gemm ptq1 {R}x{K} T={T}")
