@@ -36,6 +36,8 @@
 //     hit that XCD's L2 instead of HBM.
 //   * Tokens past the end read a valid token (the last one) and are never
 //     stored; rows past the end have zero codes and scales.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace tq {
@@ -340,8 +342,23 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
     }
     return hipSuccess;
   }
-  if (nt == 1) return launch_gemm_nt<1>(w, dm, tokens, q, dx, y, idots, s);
-  return launch_gemm_nt<2>(w, dm, tokens, q, dx, y, idots, s);
+  // One launch covers at most 2^22 workgroups (row-tile groups x token
+  // blocks, so that the grid stays far below 2^32 work-items); longer prompts
+  // go in chunks of whole token blocks, each with its tokens' activations and
+  // outputs.  The token blocking does not change the summation order.
+  const int64_t wgs_per_block = std::max<int64_t>(dm.ntiles, kBalancedWgs) + 7;
+  const int64_t chunk = std::max<int64_t>(1, (int64_t(1) << 22) / wgs_per_block) * 16 * nt;
+  for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
+    const int64_t tc = std::min(chunk, tokens - t0);
+    const int8_t* qc = q + t0 * dm.cols;
+    const float* dxc = dx ? dx + t0 * dm.nsc : nullptr;
+    float* yc = y ? y + t0 * dm.rows : nullptr;
+    int32_t* ic = idots ? idots + t0 * dm.rows * 2 * dm.nsc : nullptr;
+    const hipError_t e = nt == 1 ? launch_gemm_nt<1>(w, dm, tc, qc, dxc, yc, ic, s)
+                                 : launch_gemm_nt<2>(w, dm, tc, qc, dxc, yc, ic, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tq

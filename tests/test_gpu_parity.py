@@ -662,17 +662,20 @@ def test_max_columns(tq, orc):
         assert_close_rows(y2, yo, mag, what=f"max cols {fmt} {K} prompt")
 
 
-def test_gemm_ptq1_token_chunks(tq, orc):
-    """A ptq1_0 prompt long enough that the MFMA kernel is launched in two
-    chunks of token blocks (2^19 tokens, then 17 more: a ragged last block)."""
-    R, K, T = 3, 256, (1 << 19) + 17
+@pytest.mark.parametrize("fmt,T", [("ptq1_0", (1 << 19) + 17), ("pq2_0", 520001)])
+def test_gemm_token_chunks(tq, orc, fmt, T):
+    """Prompts long enough that the MFMA kernels are launched in two chunks of
+    token blocks: ptq1_0 2^19 tokens then 17 more; pq2_0 (one row tile,
+    2^22 workgroups per launch) 510304 tokens then 9697 more, both with a
+    ragged last block."""
+    R, K = 3, 256
     g = TI.rng(77, 19, R, K)
-    W = TI.ptq1_matrix(g, R, K)
+    W = TI.ptq1_matrix(g, R, K) if fmt == "ptq1_0" else TI.pq2_matrix(g, R, K)
     x = TI.activations(g, T, K)
-    say("gemm ptq1 token chunks", R, K, T)
-    Wd, q, d, bs, y, I = gpu_pipeline(tq, "ptq1_0", W, x)
+    say("gemm token chunks", fmt, R, K, T)
+    Wd, q, d, bs, y, I = gpu_pipeline(tq, fmt, W, x)
     qo, do, _ = orc.quantize_q8k(x)
     assert np.array_equal(q, qo)
-    assert np.array_equal(I, orc.group_dots("ptq1_0", W, qo))
-    yo, mag = orc.matmul("ptq1_0", W, qo, do, with_mag=True)
-    assert_close_rows(y, yo, mag, what=f"gemm ptq1 {R}x{K} T={T}")
+    assert np.array_equal(I, orc.group_dots(fmt, W, qo))
+    yo, mag = orc.matmul(fmt, W, qo, do, with_mag=True)
+    assert_close_rows(y, yo, mag, what=f"gemm {fmt} {R}x{K} T={T}")
