@@ -2,26 +2,45 @@
 """Benchmark of the packed-ternary x q8_K hot path on one MI355X.
 
 One step = one pass of the decode hot path over one token: q8_K quantization
-of a fresh fp32 activation vector, then the 32768 x 8192 pq2_0 matrix-vector
-product (tq_quantize_q8k + tq_gemv through the C ABI).  The weights are
-resident in HBM; eight repacked copies (570 MB) are rotated so that the
-256 MB Infinity Cache cannot serve a repeat call.
+of a fresh fp32 activation vector and the 32768 x 8192 pq2_0 matrix-vector
+product, in one launch (`tq_gemv_f32`: every workgroup quantizes the slice
+of x it needs on chip).  The weights are resident in HBM; eight repacked
+copies (570 MB) are rotated so that the 256 MB Infinity Cache cannot serve a
+repeat call.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials N]
 
-Prints ONE JSON line.  `value` is Gweights/s of the whole timed region (K
-steps captured in one HIP graph and replayed once, bracketed by
-synchronizations).  `roofline` is the matrix-vector kernel's algorithmic HBM
-bytes per launch divided by its mean duration, measured with one HIP event
-pair around K back-to-back launches of that kernel on the stream it runs on.
-`extra` carries the prompt-product (17408 x 5120, 4 and 64 tokens), 64-layer
-step and ptq1_0 figures; `cpu_baseline` times the CPU oracle on the host.
+Prints ONE JSON line.  Timing: W eager warm-up steps, then K steps captured
+in one HIP graph; the graph is replayed once untimed and then N times (N >= 5),
+each replay bracketed by stream synchronizations and timed with HIP events on
+the stream the kernels run on.  `value` is Gweights/s from the median replay;
+`ms_per_step` is that replay's time / K.  The decode step is one kernel, so
+the roofline's `kernel_us` is the same per-launch figure: the kernel's
+algorithmic HBM bytes divided by it give `achieved`.  `ceiling` holds the
+read ceiling of this part measured in the same run (libtq_probe.so): one
+streaming read of the same eight rotated 71 MB buffers, and of 1 GiB, plus the
+shader clock.  `extra` carries the prompt-product (17408 x 5120, 4 and 64
+tokens), 64-layer step, ptq1_0 and small-workload figures, each the median of
+N graph replays; `cpu_baseline` times the CPU oracle on the host.
+
+Other modes (no JSON line):
+    python bench.py --probe all|decode|prefill|ptq1|step64|...
+        the workload of the rocprofv3 counter runs: every timed kernel of the
+        benchmark launched 20 times, plus three 1 GiB device copies whose known
+        size calibrates the byte counters;
+    python bench.py --summarize DIR [--kernel-trace DIR2]
+        reads rocprofv3 CSV output (counter collection and/or kernel trace)
+        and prints the per-kernel summary committed under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -36,6 +55,9 @@ METRIC = "Gweights/s + % peak HBM GB/s, ternary GEMV 32768×8192; GMAC/s prefill
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS = 2 x MAC/s)
 MALL_BYTES = 256 << 20
+NUM_CU = 256
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc")
 
 
 def log(*a):
@@ -47,35 +69,26 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--no-extra", action="store_true", help="skip the prompt-product and ptq1_0 figures")
+    ap.add_argument("--trials", type=int, default=7, help="timed graph replays per figure (median reported; >= 5)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prompt-product, ptq1_0 and step figures")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall budget of the CPU baseline")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="only run 20 decode matrix-vector launches and three 1 GiB device copies "
-                         "(the workload of the FETCH_SIZE / WRITE_SIZE counter runs), print nothing")
+    ap.add_argument("--probe", default=None,
+                    help="run only the named workloads' kernels 20 times each (counter runs): all, decode, prefill, "
+                         "ptq1, step64, tiny, quant, ceiling (comma-separated)")
+    ap.add_argument("--summarize", default=None, help="summarize rocprofv3 counter CSVs under this directory")
+    ap.add_argument("--kernel-trace", default=None, help="with --summarize: a rocprofv3 kernel-trace CSV directory")
+    ap.add_argument("--write-counters", action="store_true",
+                    help="with --summarize: also record the per-kernel figures in profiles/counters.json")
     return ap.parse_args()
 
 
-def copies_for(nbytes: int) -> int:
-    """Enough distinct weight copies that the rotation exceeds twice the MALL."""
-    return max(2, -(-2 * MALL_BYTES // nbytes))
-
-
-def batch_us(torch, call, K):
-    """Mean duration of K back-to-back launches of call(i) on the current
-    stream: one HIP event pair around the whole batch (no host gaps between
-    the kernels, so this is the kernels' own average as a tracer sees it)."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(K):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return 1e3 * e0.elapsed_time(e1) / K
-
-
-def graph_time(torch, step, K):
-    """Capture K calls of step() in one graph, replay once; returns seconds."""
+# ----------------------------------------------------------------- timing
+def graph_trials(torch, step, K, trials):
+    """Capture K calls of step(i) in one graph; replay once untimed, then
+    `trials` times, each replay between two stream synchronizations and timed
+    with HIP events recorded on the replay stream.  Returns per-replay
+    seconds (device time) and the host wall time of each replay."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -86,22 +99,55 @@ def graph_time(torch, step, K):
     with torch.cuda.graph(g):
         for i in range(K):
             step(i)
-    g.replay()  # warm replay
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    dev_s, wall_s = [], []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(max(5, trials)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall_s.append(time.perf_counter() - t0)
+        dev_s.append(e0.elapsed_time(e1) * 1e-3)
+    del g
+    return {"median_s": statistics.median(dev_s), "min_s": min(dev_s), "max_s": max(dev_s),
+            "wall_median_s": statistics.median(wall_s), "trials": len(dev_s)}
 
 
-def decode_bench(torch, tq, K, W):
-    fmt, Wc, x = TI.make("decode_32768x8192")
+def per_call_us(t, K):
+    """Median / min / max microseconds per call of a graph_trials result."""
+    return {"us": t["median_s"] * 1e6 / K, "us_min": t["min_s"] * 1e6 / K, "us_max": t["max_s"] * 1e6 / K}
+
+
+def rounded(d, nd=4):
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def copies_for(nbytes: int) -> int:
+    """Enough distinct weight copies that the rotation exceeds twice the MALL."""
+    return max(2, -(-2 * MALL_BYTES // nbytes))
+
+
+def resident_copies(torch, tq, name):
+    """Repacked weight copies of a named workload (rotated so that no repeat
+    call is served by the Infinity Cache), and its activations."""
+    fmt, Wc, x = TI.make(name)
     R, G, _ = Wc.shape
     C = G * 128
     wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
     ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
     Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
     del wdev
+    return fmt, R, C, Ws, x
+
+
+# ----------------------------------------------------------------- workloads
+def decode_bench(torch, tq, K, W, trials):
+    fmt, R, C, Ws, _x = resident_copies(torch, tq, "decode_32768x8192")
+    ncopy = len(Ws)
     # a fresh activation vector per step: rotate over a pool of distinct vectors
     xs = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 1), 64, C)).cuda()
     q = torch.empty((1, C), dtype=torch.int8, device="cuda")
@@ -109,75 +155,65 @@ def decode_bench(torch, tq, K, W):
     bs = torch.empty((1, C // 16), dtype=torch.int16, device="cuda")
     y = torch.empty(R, dtype=torch.float32, device="cuda")
 
-    def step_two(i):
-        tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs))
-        tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
-
     def step(i):
         # one launch: every workgroup quantizes x itself, on chip
         tq.gemv_f32(fmt, Ws[i % ncopy], R, C, xs[i % 64], out=y)
 
+    def step_two(i):
+        tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs))
+        tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+
     for i in range(W):
-        step_two(i)
         step(i)
+        step_two(i)
     torch.cuda.synchronize()
-    # eager pass of whole steps (host-launched, for reference)
     t0 = time.perf_counter()
     for i in range(K):
         step(i)
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
-    # the product kernel alone, K launches back to back on this stream
-    fused_us = batch_us(torch, step, K)
-    gemv_us = batch_us(torch, lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y), K)
-    quant_us = batch_us(torch, lambda i: tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs)), K)
-    # graph passes: the timed region of `value` (fused step), and the two-kernel step
-    graph_s = graph_time(torch, step, K)
-    graph_two_s = graph_time(torch, step_two, K)
+    main = graph_trials(torch, step, K, trials)
+    two = graph_trials(torch, step_two, K, trials)
+    gemv = graph_trials(torch, lambda i: tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y), K, trials)
+    quant = graph_trials(torch, lambda i: tq.quantize_q8k(xs[i % 64: i % 64 + 1], out=(q, d, bs)), K, trials)
     wbytes = tq.repacked_bytes(fmt, R, C)
     return {
-        "R": R, "C": C, "copies": ncopy, "graph_s": graph_s, "graph_two_s": graph_two_s, "eager_s": eager_s,
-        "fused_us": fused_us, "gemv_us": gemv_us, "quant_us": quant_us,
-        # algorithmic bytes per launch: weights + fp32 x + fp32 y (fused); weights + q + d + y (two-kernel GEMV)
+        "R": R, "C": C, "Ws": Ws, "copies": ncopy, "main": main, "two": two, "gemv": gemv, "quant": quant,
+        "eager_s": eager_s,
+        # algorithmic bytes per launch: weights + fp32 x + fp32 y (fused); weights + q + d + y (stored-q8 product)
         "algo_bytes": wbytes + 4 * C + 4 * R, "algo_bytes_gemv": wbytes + C + 4 * (C // 256) + 4 * R,
         "weight_bytes": wbytes,
     }
 
 
-def prefill_bench(torch, tq, T, K, fmt_name="pq2_0"):
+def prefill_bench(torch, tq, T, K, trials, fmt_name="pq2_0"):
     prefix = "prefill" if fmt_name == "pq2_0" else "ptq1_prefill"
-    fmt, Wc, x = TI.make(f"{prefix}_17408x5120_t{T}")
-    R, G, _ = Wc.shape
-    C = G * 128
-    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
-    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
-    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
-    del wdev
+    fmt, R, C, Ws, x = resident_copies(torch, tq, f"{prefix}_17408x5120_t{T}")
+    ncopy = len(Ws)
     q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
     y = torch.empty((T, R), dtype=torch.float32, device="cuda")
-    ws = tq.workspace(fmt, R, C, T)
-    call = lambda i: tq.gemm(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y, ws=ws)
+    call = lambda i: tq.gemm(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
     for i in range(20):
         call(i)
     torch.cuda.synchronize()
-    us = graph_time(torch, call, K) * 1e6 / K  # replayed from a graph: device time, no host launch cost
+    r = per_call_us(graph_trials(torch, call, K, trials), K)
+    us = r["us"]
     macs = R * C * T
-    r = {"tokens": T, "us": us, "gmac_s": macs / us / 1e3}
-    if fmt == "pq2_0":  # int8 matrix cores; ptq1_0 takes its dot products on the vector units
-        r["mfma_frac"] = 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12)
+    r.update({"tokens": T, "gmac_s": macs / us / 1e3,
+              # int8 matrix-core share of the wall time (2 ops per MAC); the
+              # counter-based figures are under "counters"
+              "mfma_frac_wall": 2 * macs / (us * 1e-6) / (INT8_MFMA_PEAK_TOPS * 1e12)})
     bsum_bytes = 2 * T * (C // 16) if fmt == "ptq1_0" else 0
-    r["hbm_gbs"] = (tq.repacked_bytes(fmt, R, C) + T * C + bsum_bytes + 4 * T * (C // 256) + 4 * T * R) / us / 1e3
+    algo = tq.repacked_bytes(fmt, R, C) + T * C + bsum_bytes + 4 * T * (C // 256) + 4 * T * R
+    r["algo_bytes"] = algo
+    r["hbm_gbs"] = algo / us / 1e3
+    r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
     return r
 
 
-def ptq1_bench(torch, tq, K):
-    fmt, Wc, x = TI.make("ptq1_32768x8192")
-    R, G, _ = Wc.shape
-    C = G * 128
-    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
-    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
-    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
-    del wdev
+def ptq1_bench(torch, tq, K, trials):
+    fmt, R, C, Ws, x = resident_copies(torch, tq, "ptq1_32768x8192")
+    ncopy = len(Ws)
     q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
     y = torch.empty(R, dtype=torch.float32, device="cuda")
     ws = tq.workspace(fmt, R, C, 1)
@@ -185,9 +221,11 @@ def ptq1_bench(torch, tq, K):
     for i in range(20):
         call(i)
     torch.cuda.synchronize()
-    us = graph_time(torch, call, K) * 1e6 / K  # replayed from a graph
+    r = per_call_us(graph_trials(torch, call, K, trials), K)
     wb = tq.repacked_bytes(fmt, R, C)
-    return {"us": us, "gweights_s": R * C / us / 1e3, "weight_gbs": wb / us / 1e3, "hbm_frac": wb / us / 1e3 / HBM_PEAK_GBS}
+    r.update({"gweights_s": R * C / r["us"] / 1e3, "weight_gbs": wb / r["us"] / 1e3,
+              "hbm_frac": wb / r["us"] / 1e3 / HBM_PEAK_GBS})
+    return r
 
 
 def synth_pq2_gpu(torch, gen, rows, cols):
@@ -204,68 +242,79 @@ def synth_pq2_gpu(torch, gen, rows, cols):
     return torch.cat([d.view(torch.uint8).view(rows, G, 2), codes], dim=2).reshape(-1)
 
 
-def step64_bench(torch, tq, reps):
+class Step64:
     """The 64-layer decode step for one token: for each layer the gate, up,
-    down, qkv and out matrices (distinct weights, 5.7 GB in all), each
-    preceded by a fresh q8_K quantization of its own N(0,1) activation vector.
-    The 320 quantize + matrix-vector pairs are captured in one graph."""
-    fmt = "pq2_0"
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(TI.SEED_BASE + TI.STEP64)
-    mats = []
-    for layer in range(64):
-        for _name, R, C in TI.STEP64_SHAPES:
-            canon = synth_pq2_gpu(torch, gen, R, C)
-            mats.append((R, C, tq.repack(canon, fmt, R, C, check_codes=False)))
-            del canon
-    kmax = max(C for _, C, _ in mats)
-    rmax = max(R for R, _, _ in mats)
-    xs = torch.randn((len(mats), kmax), device="cuda", generator=gen)
-    q = torch.empty(kmax, dtype=torch.int8, device="cuda")
-    d = torch.empty(kmax // 256, dtype=torch.float32, device="cuda")
-    bs = torch.empty(kmax // 16, dtype=torch.int16, device="cuda")
-    y = torch.empty(rmax, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(max(tq.workspace_bytes(fmt, R, C) for R, C, _ in mats), dtype=torch.uint8, device="cuda")
+    down, qkv and out matrices (distinct weights, 5.7 GB in all), each with a
+    fresh q8_K quantization of its own N(0,1) activation vector.  Gate and up
+    share one launch (tq_gemv_f32_batch); the others are tq_gemv_f32."""
 
-    def step_two(_i):
-        for m, (R, C, Wd) in enumerate(mats):
-            tq.quantize_q8k(xs[m, :C].view(1, C), out=(q[:C].view(1, C), d[: C // 256].view(1, -1), bs[: C // 16].view(1, -1)))
-            tq.gemv(fmt, Wd, R, C, q[:C], d[: C // 256], bs[: C // 16], out=y[:R], ws=ws)
+    def __init__(self, torch, tq):
+        self.torch, self.tq = torch, tq
+        fmt = self.fmt = "pq2_0"
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(TI.SEED_BASE + TI.STEP64)
+        self.mats = []
+        for _layer in range(64):
+            for _name, R, C in TI.STEP64_SHAPES:
+                canon = synth_pq2_gpu(torch, gen, R, C)
+                self.mats.append((R, C, tq.repack(canon, fmt, R, C, check_codes=False)))
+                del canon
+        self.names = [name for _layer in range(64) for name, _R, _C in TI.STEP64_SHAPES]
+        kmax = max(C for _, C, _ in self.mats)
+        rmax = max(R for R, _, _ in self.mats)
+        self.xs = torch.randn((len(self.mats), kmax), device="cuda", generator=gen)
+        self.q = torch.empty(kmax, dtype=torch.int8, device="cuda")
+        self.d = torch.empty(kmax // 256, dtype=torch.float32, device="cuda")
+        self.bs = torch.empty(kmax // 16, dtype=torch.int16, device="cuda")
+        self.y = torch.empty(rmax, dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(max(tq.workspace_bytes(fmt, R, C) for R, C, _ in self.mats), dtype=torch.uint8,
+                              device="cuda")
+        self.ys = [torch.empty(R, dtype=torch.float32, device="cuda") for R, _C, _W in self.mats[:2]]
+        pair_rows = sum(-(-R // 64) * 64 for R, _C, _W in self.mats[:2])
+        self.ws_pair = torch.zeros(max(16, tq.workspace_bytes(fmt, pair_rows, self.mats[0][1])), dtype=torch.uint8,
+                                   device="cuda")
 
-    names = [name for _layer in range(64) for name, _R, _C in TI.STEP64_SHAPES]
-    ys = [torch.empty(R, dtype=torch.float32, device="cuda") for R, _C, _W in mats[:2]]
-    ws_pair = torch.zeros(max(16, tq.workspace_bytes(fmt, sum(-(-R // 64) * 64 for R, _C, _W in mats[:2]), mats[0][1])),
-                          dtype=torch.uint8, device="cuda")
-
-    def step(_i):
+    def step(self, _i=0):
+        tq, fmt, mats, names = self.tq, self.fmt, self.mats, self.names
         m = 0
         while m < len(mats):
             R, C, Wd = mats[m]
             if names[m] == "gate" and names[m + 1] == "up":
                 # gate and up read the same layer input in a real model: one launch
                 R2, _C2, Wd2 = mats[m + 1]
-                tq.gemv_f32_batch(fmt, [Wd, Wd2], [R, R2], C, [xs[m, :C], xs[m + 1, :C]], outs=ys, ws=ws_pair)
+                tq.gemv_f32_batch(fmt, [Wd, Wd2], [R, R2], C, [self.xs[m, :C], self.xs[m + 1, :C]], outs=self.ys,
+                                  ws=self.ws_pair)
                 m += 2
                 continue
-            tq.gemv_f32(fmt, Wd, R, C, xs[m, :C], out=y[:R], ws=ws)
+            tq.gemv_f32(fmt, Wd, R, C, self.xs[m, :C], out=self.y[:R], ws=self.ws)
             m += 1
 
-    step_two(0)
-    step(0)
+    def step_two(self, _i=0):
+        tq, fmt = self.tq, self.fmt
+        for m, (R, C, Wd) in enumerate(self.mats):
+            tq.quantize_q8k(self.xs[m, :C].view(1, C), out=(self.q[:C].view(1, C), self.d[: C // 256].view(1, -1),
+                                                             self.bs[: C // 16].view(1, -1)))
+            tq.gemv(fmt, Wd, R, C, self.q[:C], self.d[: C // 256], self.bs[: C // 16], out=self.y[:R], ws=self.ws)
+
+
+def step64_bench(torch, tq, reps, trials):
+    s = Step64(torch, tq)
+    s.step_two()
+    s.step()
     torch.cuda.synchronize()
-    g_s = graph_time(torch, step, reps)
-    g2_s = graph_time(torch, step_two, reps)
-    weights = sum(R * C for R, C, _ in mats)
-    wbytes = sum(tq.repacked_bytes(fmt, R, C) for R, C, _ in mats)
-    ms = g_s * 1e3 / reps
-    return {"matrices": len(mats), "step": "tq_gemv_f32_batch for gate + up, tq_gemv_f32 for down, qkv, out",
-            "ms_per_token": ms,
+    t = graph_trials(torch, s.step, reps, trials)
+    t2 = graph_trials(torch, s.step_two, reps, trials)
+    weights = sum(R * C for R, C, _ in s.mats)
+    wbytes = sum(tq.repacked_bytes(s.fmt, R, C) for R, C, _ in s.mats)
+    ms = t["median_s"] * 1e3 / reps
+    return {"matrices": len(s.mats), "step": "tq_gemv_f32_batch for gate + up, tq_gemv_f32 for down, qkv, out",
+            "ms_per_token": ms, "ms_min": t["min_s"] * 1e3 / reps, "ms_max": t["max_s"] * 1e3 / reps,
             "gweights_s": weights / (ms * 1e-3) / 1e9,
             "weight_gbs": wbytes / (ms * 1e-3) / 1e9, "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "weight_bytes": wbytes, "two_kernel_ms_per_token": g2_s * 1e3 / reps}
+            "weight_bytes": wbytes, "two_kernel_ms_per_token": t2["median_s"] * 1e3 / reps}
 
 
-def tiny_bench(torch, tq, K):
+def tiny_bench(torch, tq, K, trials):
     """The 256x1024 workload: one fused call per step, replayed from a graph
     (launch-bound: its 70 KB of weights stay in the caches)."""
     fmt, Wc, x = TI.make("tiny_256x1024")
@@ -275,107 +324,312 @@ def tiny_bench(torch, tq, K):
     xd = torch.from_numpy(x[0].copy()).cuda()
     y = torch.empty(R, dtype=torch.float32, device="cuda")
     ws = tq.workspace(fmt, R, C, 1)
-    step = lambda i: tq.gemv_f32(fmt, W, R, C, xd, out=y, ws=ws)
-    t = graph_time(torch, step, K)
-    return {"rows": R, "cols": C, "us_per_step": t * 1e6 / K, "gweights_s": R * C * K / t / 1e9}
+    r = per_call_us(graph_trials(torch, lambda i: tq.gemv_f32(fmt, W, R, C, xd, out=y, ws=ws), K, trials), K)
+    r.update({"rows": R, "cols": C, "gweights_s": R * C / r["us"] / 1e3})
+    return r
 
 
-def quantize_bench(torch, tq, K):
+def quantize_bench(torch, tq, K, trials):
     C = 8192
     xs = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 2), 1, C)).cuda()
     out = (torch.empty((1, C), dtype=torch.int8, device="cuda"), torch.empty((1, 32), dtype=torch.float32, device="cuda"),
            torch.empty((1, 512), dtype=torch.int16, device="cuda"))
-    for _ in range(20):
-        tq.quantize_q8k(xs, out=out)
-    torch.cuda.synchronize()
-    us = batch_us(torch, lambda i: tq.quantize_q8k(xs, out=out), K)
-    # replayed from a graph: the kernel's cadence without the host's launch cost
-    graph_us = graph_time(torch, lambda i: tq.quantize_q8k(xs, out=out), K) * 1e6 / K
-    return {"cols": C, "us": us, "graph_us": graph_us}
+    r = per_call_us(graph_trials(torch, lambda i: tq.quantize_q8k(xs, out=out), K, trials), K)
+    r["cols"] = C
+    return r
 
 
-def ceiling_probe(torch):
-    """Plain streaming kernels of known size: torch's sum (read) and copy."""
-    n = (2 << 30) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+# ----------------------------------------------------------------- ceiling probe
+def probe_lib():
+    import ctypes
+
+    import bit_quantized_matvec_amd as tq  # noqa: F401  (loads torch's HIP runtime first)
+
+    path = os.path.join(ROOT, "bit_quantized_matvec_amd", "libtq_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python bit_quantized_matvec_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.tqp_read.argtypes = [P, I64, I, I, I, P, P]
+    lib.tqp_read.restype = I
+    lib.tqp_clock.argtypes = [P, I, I, P, I64, P]
+    lib.tqp_clock.restype = I
+    return lib
+
+
+READ_BLOCKS, READ_THREADS = 8192, 512  # the fastest shape of a sweep of the read kernel
+
+
+def ceiling_bench(torch, bufs, K, trials):
+    """Streaming reads with libtq_probe's read kernel: one pass over each of the
+    rotated 71 MB weight copies (the decode step's own buffers, so the same
+    one-shot, cache-cold traffic), and over a 1 GiB buffer; plus the shader
+    clock (s_memtime against the 100 MHz s_memrealtime), idle and while
+    streaming."""
+    import ctypes
+
+    lib = probe_lib()
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def read(buf, nt=1):
+        st = lib.tqp_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), READ_BLOCKS,
+                          READ_THREADS, nt, ctypes.c_void_p(sink.data_ptr()), stream())
+        if st != 0:
+            raise RuntimeError(f"tqp_read failed: hipError {st}")
+
+    nb = bufs[0].numel()
+    for i in range(16):
+        read(bufs[i % len(bufs)])
+    r71 = per_call_us(graph_trials(torch, lambda i: read(bufs[i % len(bufs)]), K, trials), K)
+    r71_c = per_call_us(graph_trials(torch, lambda i: read(bufs[i % len(bufs)], 0), K, trials), K)
+    big = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
     for _ in range(3):
-        a.sum()
-        b.copy_(a[: n // 2])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        a.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    read_gbs = 10 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    e0.record()
-    for _ in range(10):
-        b.copy_(a[: n // 2])
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 10 * 2 * 4 * (n // 2) / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, b
-    return {"read_sum_2GiB_gbs": read_gbs, "copy_1GiB_gbs": copy_gbs}
+        read(big)
+    rbig = per_call_us(graph_trials(torch, lambda i: read(big), 10, trials), 10)
+    # clock
+    blocks = 2048
+    out = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    mhz = {}
+    for label, iters, buf in (("spin", 200000, None), ("streaming", 400, big)):
+        for _ in range(2):
+            st = lib.tqp_clock(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                               ctypes.c_void_p(buf.data_ptr()) if buf is not None else None,
+                               buf.numel() * 4 if buf is not None else 0, stream())
+            if st != 0:
+                raise RuntimeError(f"tqp_clock failed: hipError {st}")
+        torch.cuda.synchronize()
+        h = out.cpu().numpy().reshape(blocks, 2).astype(np.float64)
+        mhz[label] = float(np.median(100.0 * h[:, 0] / np.maximum(h[:, 1], 1)))
+    del big
+    return {"read_71MB_rotated_us": r71["us"], "read_71MB_rotated_gbs": nb / r71["us"] / 1e3,
+            "read_71MB_rotated_cached_loads_gbs": nb / r71_c["us"] / 1e3,
+            "read_1GiB_gbs": (1 << 30) / rbig["us"] / 1e3,
+            "read_shape": f"{READ_BLOCKS} workgroups x {READ_THREADS} threads, 4 x 16 B non-temporal loads in flight per thread",
+            "sclk_mhz_spin": mhz["spin"], "sclk_mhz_streaming": mhz["streaming"]}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_32768x8192.json")
-# the sources the decode kernel is compiled from: the recorded traffic holds while their hash matches
-GEMV_SOURCES = [os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", f) for f in ("k_gemv_pq2.hip", "q8k_block.h")]
+# ----------------------------------------------------------------- counters on record
+def source_sha256(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
-def traffic_probe(torch, tq):
-    """The workload of the HBM-traffic counter runs: 20 launches of the
-    decode product with quantization inside (the timed step), then 20 of the
-    matrix-vector kernel on a stored q8_K vector (rotating weight copies, as
-    in the timed run), and three device-to-device copies of 1 GiB, whose
-    known byte count calibrates the counters."""
-    fmt, Wc, x = TI.make("decode_32768x8192")
-    R, G, _ = Wc.shape
-    C = G * 128
-    wdev = torch.from_numpy(Wc.reshape(-1)).cuda()
-    ncopy = copies_for(tq.repacked_bytes(fmt, R, C))
-    Ws = [tq.repack(wdev, fmt, R, C) for _ in range(ncopy)]
-    del wdev
-    xd = torch.from_numpy(x).cuda()
-    q, d, bs = tq.quantize_q8k(xd)
-    y = torch.empty(R, dtype=torch.float32, device="cuda")
-    for i in range(20):
-        tq.gemv_f32(fmt, Ws[i % ncopy], R, C, xd[0], out=y)
-    for i in range(20):
-        tq.gemv(fmt, Ws[i % ncopy], R, C, q, d, bs, out=y)
+# the sources each benchmarked kernel is compiled from: a recorded counter
+# figure is reported only while their hash matches
+KERNEL_SOURCES = {
+    "gemv_pq2_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h"],
+    "gemv_pq2_batch_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h"],
+    "gemm_pq2_kernel": ["k_gemm_pq2.hip", "kernels.h", "layout.h"],
+    "gemv_ptq1_kernel": ["k_gemv_ptq1.hip", "kernels.h", "layout.h"],
+    "gemm_ptq1_kernel": ["k_gemm_ptq1.hip", "kernels.h", "layout.h"],
+    "quantize_q8k_kernel": ["k_quant.hip", "q8k_block.h", "kernels.h"],
+}
+
+
+def kernel_family(name: str):
+    for fam in KERNEL_SOURCES:
+        if f"{fam}<" in name or f"{fam}(" in name or name.endswith(fam):
+            return fam
+    return None
+
+
+def recorded_counters():
+    """Per-kernel counter figures from the committed counter runs whose
+    kernel sources still hash the same, keyed by label; {} if none."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    for label, e in rec.get("kernels", {}).items():
+        fam = e.get("family")
+        if fam in KERNEL_SOURCES and e.get("source_sha256") == source_sha256(KERNEL_SOURCES[fam]):
+            out[label] = e
+    return out
+
+
+# ----------------------------------------------------------------- counter-run workload
+def probe_workloads(torch, tq, names):
+    """Every benchmarked kernel 20 times (what the counter runs profile), then
+    three device copies of 1 GiB that calibrate the byte counters."""
+    names = set(names.split(","))
+    every = "all" in names
+    n = 20
+    if every or "decode" in names:
+        log("probe: decode")
+        fmt, R, C, Ws, x = resident_copies(torch, tq, "decode_32768x8192")
+        xd = torch.from_numpy(x).cuda()
+        q, d, bs = tq.quantize_q8k(xd)
+        y = torch.empty(R, dtype=torch.float32, device="cuda")
+        for i in range(n):
+            tq.gemv_f32(fmt, Ws[i % len(Ws)], R, C, xd[0], out=y)
+        for i in range(n):
+            tq.gemv(fmt, Ws[i % len(Ws)], R, C, q, d, bs, out=y)
+        if every or "ceiling" in names:
+            lib = probe_lib()
+            import ctypes
+
+            sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+            for i in range(n):
+                lib.tqp_read(ctypes.c_void_p(Ws[i % len(Ws)].data_ptr()), Ws[0].numel(), READ_BLOCKS, READ_THREADS, 1,
+                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        del Ws
+    if every or "quant" in names:
+        log("probe: quantize")
+        x = torch.from_numpy(TI.activations(TI.rng(TI.DECODE, 0, 0, 2), 1, 8192)).cuda()
+        for _ in range(n):
+            tq.quantize_q8k(x)
+    if every or "prefill" in names:
+        for T in (4, 64):
+            log(f"probe: prefill t{T}")
+            fmt, R, C, Ws, x = resident_copies(torch, tq, f"prefill_17408x5120_t{T}")
+            q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+            y = torch.empty((T, R), dtype=torch.float32, device="cuda")
+            for i in range(n):
+                tq.gemm(fmt, Ws[i % len(Ws)], R, C, q, d, bs, out=y)
+            torch.cuda.synchronize()
+            del Ws
+    if every or "ptq1" in names:
+        log("probe: ptq1")
+        fmt, R, C, Ws, x = resident_copies(torch, tq, "ptq1_32768x8192")
+        q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+        y = torch.empty(R, dtype=torch.float32, device="cuda")
+        ws = tq.workspace(fmt, R, C, 1)
+        for i in range(n):
+            tq.gemv(fmt, Ws[i % len(Ws)], R, C, q, d, bs, out=y, ws=ws)
+        torch.cuda.synchronize()
+        del Ws
+        for T in (4, 64):
+            log(f"probe: ptq1 prefill t{T}")
+            fmt, R, C, Ws, x = resident_copies(torch, tq, f"ptq1_prefill_17408x5120_t{T}")
+            q, d, bs = tq.quantize_q8k(torch.from_numpy(x).cuda())
+            y = torch.empty((T, R), dtype=torch.float32, device="cuda")
+            for i in range(n):
+                tq.gemm(fmt, Ws[i % len(Ws)], R, C, q, d, bs, out=y)
+            torch.cuda.synchronize()
+            del Ws
+    if every or "tiny" in names:
+        log("probe: tiny")
+        fmt, Wc, x = TI.make("tiny_256x1024")
+        R, G, _ = Wc.shape
+        C = G * 128
+        W = tq.repack(torch.from_numpy(Wc.reshape(-1)).cuda(), fmt, R, C)
+        xd = torch.from_numpy(x[0].copy()).cuda()
+        y = torch.empty(R, dtype=torch.float32, device="cuda")
+        ws = tq.workspace(fmt, R, C, 1)
+        for _ in range(n):
+            tq.gemv_f32(fmt, W, R, C, xd, out=y, ws=ws)
+    if every or "step64" in names:
+        log("probe: step64")
+        s = Step64(torch, tq)
+        for _ in range(2):
+            s.step()
+        torch.cuda.synchronize()
+        del s
     torch.cuda.synchronize()
-    n = (1 << 30) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty(n, dtype=torch.float32, device="cuda")
+    log("probe: 1 GiB copies")
+    a = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
 
 
-def kernel_source_sha256() -> str:
-    import hashlib
-
-    h = hashlib.sha256()
-    for path in GEMV_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def recorded_traffic():
-    """HBM bytes per launch of the decode kernel from the committed counter
-    runs, or None if the kernel sources changed since they were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-        sha = kernel_source_sha256()
-    except (OSError, ValueError):
-        return None
-    return rec.get("traffic_bytes") if rec.get("kernel_source_sha256") == sha else None
+# ----------------------------------------------------------------- rocprofv3 summaries
+def _read_csvs(d, suffix):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
 
 
+def short_name(name: str) -> str:
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.replace("tq::(anonymous namespace)::", "tq::").replace("(anonymous namespace)::", "")
+    cut = name.find("(")
+    return name[:cut] if cut > 0 else name
+
+
+def summarize(counter_dir, trace_dir=None):
+    """Median counter value per (kernel, grid) from rocprofv3 counter-collection
+    CSVs; byte counters scaled by what they read for the 1 GiB device copy;
+    derived MFMA / VALU / LDS figures; durations from a kernel-trace CSV."""
+    rows = _read_csvs(counter_dir, "counter_collection.csv") if counter_dir else []
+    vals = {}
+    for r in rows:
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]), int(r["LDS_Block_Size"]))
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+    # calibration: the 1 GiB copy reads and writes exactly 2^30 bytes
+    copy = [cs for k, cs in med.items() if "copyBuffer" in k[0]]  # the largest reading is the 1 GiB copy
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        got = [cs[c] for cs in copy if c in cs]
+        if got:
+            scale[c] = (1 << 30) / (max(got) * 1024.0)
+    durations = {}
+    if trace_dir:
+        for r in _read_csvs(trace_dir, "kernel_trace.csv"):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]), int(r["LDS_Block_Size"]))
+            durations.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    out = {}
+    for key in sorted(set(med) | set(durations), key=lambda k: (k[0], k[1])):
+        fam = kernel_family(key[0])
+        if fam is None and "copyBuffer" not in key[0] and "read_kernel" not in key[0]:
+            continue
+        cs = med.get(key, {})
+        e = {"kernel": key[0], "grid": key[1], "block": key[2], "lds": key[3], "family": fam}
+        for c, v in cs.items():
+            e[c] = v
+        if "FETCH_SIZE" in cs and "FETCH_SIZE" in scale:
+            e["fetch_bytes"] = cs["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+        if "WRITE_SIZE" in cs and "WRITE_SIZE" in scale:
+            e["write_bytes"] = cs["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+        gui = cs.get("GRBM_GUI_ACTIVE")
+        if gui:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+                # share of the CUs' matrix-core cycles that were busy while the GPU was active
+                e["mfma_busy_frac"] = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * NUM_CU * 4)
+            if "SQ_ACTIVE_INST_VALU" in cs:
+                e["valu_active_frac"] = cs["SQ_ACTIVE_INST_VALU"] / (gui * NUM_CU * 4)
+            if "SQ_BUSY_CYCLES" in cs:
+                e["sq_busy_frac"] = cs["SQ_BUSY_CYCLES"] / gui
+        if key in durations:
+            ds = durations[key]
+            e["trace_launches"] = len(ds)
+            e["trace_avg_us"] = sum(ds) / len(ds)
+            e["trace_median_us"] = statistics.median(ds)
+        if fam:
+            e["source_sha256"] = source_sha256(KERNEL_SOURCES[fam])
+        out[f"{key[0]} grid={key[1]} block={key[2]}"] = e
+    return {"scale": scale, "kernels": out}
+
+
+def print_summary(s):
+    cols = ["fetch_bytes", "write_bytes", "SQ_INSTS_VALU_MFMA_MOPS_I8", "mfma_busy_frac", "valu_active_frac",
+            "SQ_INSTS_VALU", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "VALUBusy", "trace_avg_us"]
+    present = [c for c in cols if any(c in e for e in s["kernels"].values())]
+    print("byte-counter scale (bytes per KiB read):", {k: round(v, 6) for k, v in s["scale"].items()})
+    print()
+    print("| kernel | grid / block | " + " | ".join(present) + " |")
+    print("|---|---|" + "---|" * len(present))
+    for e in s["kernels"].values():
+        cells = []
+        for c in present:
+            v = e.get(c)
+            cells.append("" if v is None else (f"{v:.4g}" if isinstance(v, float) else str(v)))
+        print(f"| {e['kernel']} | {e['grid']} / {e['block']} | " + " | ".join(cells) + " |")
+
+
+# ----------------------------------------------------------------- CPU oracle
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -419,17 +673,14 @@ def cpu_baseline(seconds: float):
                      f"row ranges split over {cores} threads",
            "cpu": _cpu_model(), "cflags": " ".join(oracle.CFLAGS)}
     side = seconds / 3
-    # one core, the first 4096 rows of the same product
     q1, d1, _ = oracle.quantize_q8k(x)
     n, dt = run(lambda: oracle.matmul(fmt, Wc, q1, d1, rows=(0, 4096), threads=1), side)
     out["one_core_gweights_s"] = n * 4096 * G * 128 / dt / 1e9
-    # ptq1_0 32768 x 8192 on all cores
     pfmt, Pc, px = TI.make("ptq1_32768x8192")
     pq, pd, _ = oracle.quantize_q8k(px)
     n, dt = run(lambda: oracle.matmul(pfmt, Pc, pq, pd, threads=cores), side)
     out["ptq1_gweights_s"] = n * Pc.shape[0] * Pc.shape[1] * 128 / dt / 1e9
     del Pc
-    # prompt product 17408 x 5120, 64 tokens, a block of 1024 rows on all cores
     gfmt, Gc, gx = TI.make("prefill_17408x5120_t64")
     gq, gd, _ = oracle.quantize_q8k(gx)
     sub = np.ascontiguousarray(Gc[:1024])
@@ -438,8 +689,17 @@ def cpu_baseline(seconds: float):
     return out
 
 
+# ----------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.summarize:
+        s = summarize(args.summarize, args.kernel_trace)
+        print_summary(s)
+        if args.write_counters:
+            s["command_note"] = "see the profiles/*.md summaries for the rocprofv3 commands"
+            with open(COUNTERS_FILE, "w") as f:
+                json.dump(s, f, indent=1, sort_keys=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
               file=sys.stderr)
@@ -451,14 +711,29 @@ def main():
         sys.exit(2)
     import bit_quantized_matvec_amd as tq
 
-    if args.traffic_probe:
-        traffic_probe(torch, tq)
+    if args.probe:
+        probe_workloads(torch, tq, args.probe)
         return
+    trials = max(5, args.trials)
+    K = args.steps
     log("decode bench")
-    dec = decode_bench(torch, tq, args.steps, args.warmup)
-    R, C, K = dec["R"], dec["C"], args.steps
-    value = K * R * C / dec["graph_s"] / 1e9
-    achieved = dec["algo_bytes"] / (dec["fused_us"] * 1e-6) / 1e9
+    dec = decode_bench(torch, tq, K, args.warmup, trials)
+    R, C = dec["R"], dec["C"]
+    main_t = dec["main"]
+    step_s = main_t["median_s"]
+    value = K * R * C / step_s / 1e9
+    kernel_us = step_s * 1e6 / K  # the step is one kernel launch
+    achieved = dec["algo_bytes"] / (kernel_us * 1e-6) / 1e9
+    log("ceiling probe")
+    ceil = ceiling_bench(torch, dec["Ws"], min(K, 1000), trials)
+    del dec["Ws"]
+    counters = recorded_counters()
+    fused = {k: v for k, v in counters.items() if v.get("family") == "gemv_pq2_kernel" and v.get("grid") == 131072
+             and v.get("lds", 0) > 16384}
+    traffic = None
+    for v in fused.values():
+        if "fetch_bytes" in v and "write_bytes" in v:
+            traffic = round(v["fetch_bytes"] + v["write_bytes"])
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -466,7 +741,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["graph_s"] * 1e3 / K, 5),
+        "ms_per_step": round(step_s * 1e3 / K, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -474,36 +749,44 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_32768x8192", "format": "pq2_0", "rows": R, "cols": C, "tokens": 1,
                    "step": "tq_gemv_f32 (q8_K quantization inside the product kernel)",
-                   "weight_copies_rotated": dec["copies"], "timing": "hip graph of K steps"},
+                   "weight_copies_rotated": dec["copies"],
+                   "timing": f"hip graph of K steps, median of {main_t['trials']} replays timed with HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "gemv_pq2_kernel (fused q8_K)", "kernel_us": round(dec["fused_us"], 3),
-                     "algo_bytes": dec["algo_bytes"]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "gemv_pq2_kernel (fused q8_K)", "kernel_us": round(kernel_us, 3),
+                     "kernel_us_min": round(main_t["min_s"] * 1e6 / K, 3),
+                     "kernel_us_max": round(main_t["max_s"] * 1e6 / K, 3),
+                     "algo_bytes": dec["algo_bytes"],
+                     "frac_of_measured_ceiling": round(ceil["read_71MB_rotated_us"] / kernel_us, 4)},
     }
-    extra = {"decode_eager_gweights_s": round(K * R * C / dec["eager_s"] / 1e9, 2),
-             "decode_two_kernel_step": {"step": "tq_quantize_q8k + tq_gemv",
-                                        "gweights_s": round(K * R * C / dec["graph_two_s"] / 1e9, 2),
-                                        "us_per_step": round(dec["graph_two_s"] * 1e6 / K, 3),
-                                        "gemv_us": round(dec["gemv_us"], 3), "quant_us": round(dec["quant_us"], 3),
-                                        "gemv_hbm_frac": round(dec["algo_bytes_gemv"] / (dec["gemv_us"] * 1e-6) / 1e9
-                                                               / HBM_PEAK_GBS, 4)},
-             "decode_weight_gbs": round(dec["weight_bytes"] / (dec["fused_us"] * 1e-6) / 1e9, 1),
-             "decode_kernel_gweights_s": round(R * C / dec["fused_us"] / 1e3, 1)}
+    extra = {"decode_wall_gweights_s": round(K * R * C / main_t["wall_median_s"] / 1e9, 2),
+             "decode_eager_gweights_s": round(K * R * C / dec["eager_s"] / 1e9, 2),
+             "decode_two_kernel_step": rounded({
+                 "step": "tq_quantize_q8k + tq_gemv",
+                 "gweights_s": K * R * C / dec["two"]["median_s"] / 1e9,
+                 "us_per_step": dec["two"]["median_s"] * 1e6 / K,
+                 "gemv_us": dec["gemv"]["median_s"] * 1e6 / K,
+                 "quant_us": dec["quant"]["median_s"] * 1e6 / K,
+                 "gemv_hbm_frac": dec["algo_bytes_gemv"] / (dec["gemv"]["median_s"] / K) / 1e9 / HBM_PEAK_GBS}),
+             "decode_weight_gbs": round(dec["weight_bytes"] / (kernel_us * 1e-6) / 1e9, 1),
+             "ceiling": rounded(ceil, 3)}
     if not args.no_extra:
-        log("prefill / ptq1 / quantize / ceiling")
+        log("prefill")
         for T in (4, 64):
-            p = prefill_bench(torch, tq, T, 200)
-            extra[f"prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
+            extra[f"prefill_t{T}"] = rounded(prefill_bench(torch, tq, T, 200, trials))
         log("64-layer step")
-        extra["step64"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in step64_bench(torch, tq, 5).items()}
-        p = ptq1_bench(torch, tq, 200)
-        extra["ptq1_decode"] = {k: round(v, 4) for k, v in p.items()}
+        extra["step64"] = rounded(step64_bench(torch, tq, 5, trials))
+        log("ptq1")
+        extra["ptq1_decode"] = rounded(ptq1_bench(torch, tq, 200, trials))
         for T in (4, 64):
-            p = prefill_bench(torch, tq, T, 100, "ptq1_0")
-            extra[f"ptq1_prefill_t{T}"] = {k: round(v, 4) if isinstance(v, float) else v for k, v in p.items()}
-        extra["quantize_8192"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in quantize_bench(torch, tq, 200).items()}
-        extra["tiny_256x1024"] = {k: round(v, 3) if isinstance(v, float) else v for k, v in tiny_bench(torch, tq, 1000).items()}
-        extra["ceiling"] = {k: round(v, 1) for k, v in ceiling_probe(torch).items()}
+            extra[f"ptq1_prefill_t{T}"] = rounded(prefill_bench(torch, tq, T, 100, trials, "ptq1_0"))
+        extra["quantize_8192"] = rounded(quantize_bench(torch, tq, 200, trials), 3)
+        extra["tiny_256x1024"] = rounded(tiny_bench(torch, tq, 1000, trials), 3)
+    if counters:
+        extra["counters"] = {k: rounded({c: v[c] for c in ("fetch_bytes", "write_bytes", "mfma_busy_frac",
+                                                          "valu_active_frac", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                                                          "trace_avg_us") if c in v}, 4)
+                             for k, v in counters.items()}
     out["extra"] = extra
     if not args.no_cpu:
         log("cpu baseline")

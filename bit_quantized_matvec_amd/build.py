@@ -16,9 +16,13 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
+# measurement kernels of the benchmark (HBM read ceiling, shader clock), kept
+# out of the product library
+PROBE_LIB = os.path.join(HERE, "libtq_probe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["tq_api.cpp", "k_quant.hip", "k_repack.hip", "k_gemv_pq2.hip", "k_gemm_pq2.hip", "k_gemv_ptq1.hip", "k_gemm_ptq1.hip"]
+SOURCES = ["tq_api.cpp", "k_workspace.hip", "k_quant.hip", "k_repack.hip", "k_gemv_pq2.hip", "k_gemm_pq2.hip", "k_gemv_ptq1.hip", "k_gemm_ptq1.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -49,8 +53,14 @@ def build(verbose: bool = False) -> str:
         tmp_lib = LIB + ".tmp"
         subprocess.check_call([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
+        pobjs = [os.path.join(tmp, s + ".o") for s in PROBE_SOURCES]
+        for src, obj in zip(PROBE_SOURCES, pobjs):
+            _compile(src, obj)
+        tmp_lib = PROBE_LIB + ".tmp"
+        subprocess.check_call([HIPCC, "-shared", f"--offload-arch={ARCH}", *pobjs, "-o", tmp_lib])
+        os.replace(tmp_lib, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

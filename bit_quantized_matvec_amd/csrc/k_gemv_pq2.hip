@@ -36,8 +36,8 @@
 namespace tq {
 namespace {
 
-constexpr int kMaxWaves = 16;  // the kernel's limit
-constexpr int kPlanWaves = 4;  // what the plan uses
+constexpr int kPlanWaves = 4;  // waves per workgroup (at most)
+constexpr int kMaxWaves = kPlanWaves;
 constexpr size_t kMaxStageBytes = 32 * 1024;  // LDS for one slice's staged activations
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -205,12 +205,14 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
       for (int i = 0; i < kXB; ++i) v[i] = xf[(size_t)(wg0 + min(b0 + wave + i * nw, nb - 1)) * 64 + lane];
     };
     auto quant_batch = [&](int b0) {
+      float db[kXB];
+      int pk[kXB];
+      q8k_quant_batch<kXB>(v, db, pk);
 #pragma unroll
       for (int i = 0; i < kXB; ++i) {
         const int b = min(b0 + wave + i * nw, nb - 1);
-        const float db = q8k_block_scale(v[i]);
-        stage[b * 64 + lane] = q8k_quant4(v[i], db);
-        if (lane == 0) sd[b] = db;
+        stage[b * 64 + lane] = pk[i];
+        if (lane == 0) sd[b] = db[i];
       }
     };
     load_batch(0);
@@ -282,8 +284,10 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Launch bounds: at most kMaxWaves waves, and two workgroups per compute unit
+// (the decode grid of 512 row tiles on 256 compute units), so up to 256 VGPRs.
 template <int RING, bool IDOTS, bool NT, bool LDSQ, bool FX, int XB = 1>
-__global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* __restrict__ codes,
+__global__ __launch_bounds__(64 * kMaxWaves, 2) void gemv_pq2_kernel(const uint4* __restrict__ codes,
                                                                   const uint32_t* __restrict__ scales,
                                                                   const int* __restrict__ q, const float* __restrict__ dx,
                                                                   const float4* __restrict__ xf,
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_kernel(const uint4* _
 // Several independent fused products with the same column count in one
 // launch: workgroup x belongs to problem m with tile0[m] <= x < tile0[m + 1].
 template <int XB>
-__global__ __launch_bounds__(64 * kMaxWaves) void gemv_pq2_batch_kernel(GemvBatch b, int nsc, int G8, int scw, int spw,
+__global__ __launch_bounds__(64 * kMaxWaves, 2) void gemv_pq2_batch_kernel(GemvBatch b, int nsc, int G8, int scw, int spw,
                                                                         uint8_t* __restrict__ ws) {
   const int x = blockIdx.x;
   int m = 0;

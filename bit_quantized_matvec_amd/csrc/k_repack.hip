@@ -13,8 +13,18 @@ namespace tq {
 namespace {
 
 constexpr int kThreads = 256;
+// Every kernel below loops over its items with a grid stride, so a launch
+// covers any item count with at most kMaxBlocks workgroups (2^28 work-items,
+// far below the 2^32 limit of one launch dimension).
+constexpr int64_t kMaxBlocks = int64_t(1) << 20;
 
-inline unsigned grid_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+inline unsigned grid_for(int64_t n) {
+  const int64_t b = (n + kThreads - 1) / kThreads;
+  return (unsigned)(b < kMaxBlocks ? (b > 0 ? b : 1) : kMaxBlocks);
+}
+
+#define TQ_FOR_ITEMS(i, n) \
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < (n); i += (int64_t)gridDim.x * kThreads)
 
 // ---------------------------------------------------------------- pq2_0 codes
 // Output dword index i -> (tile, sc, qd, row, c).  Its byte j, field s holds
@@ -25,8 +35,7 @@ inline unsigned grid_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kTh
 // field re-coded from u = w + 1 to two's-complement w.
 __global__ void repack_pq2_codes(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows, int64_t nsc,
                                  int64_t ndw, int32_t* __restrict__ bad_flag) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= ndw) return;
+  TQ_FOR_ITEMS(i, ndw) {
   const int c = (int)(i & 3);
   const int r = (int)((i >> 2) & 63);
   const int qd = (int)((i >> 8) & 3);
@@ -54,14 +63,14 @@ __global__ void repack_pq2_codes(const uint8_t* __restrict__ src, uint32_t* __re
     if (bad && bad_flag) *bad_flag = 1;
   }
   dst[i] = out;
+  }
 }
 
 // Inverse: one thread per canonical 34-byte block.
 __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ scales,
                                    uint8_t* __restrict__ dst, int64_t rows, int64_t nsc) {
   const int64_t G = nsc * 2;
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= rows * G) return;
+  TQ_FOR_ITEMS(b, rows * G) {
   const int64_t row = b / G, g = b % G;
   const int64_t tile = row / kRowTile;
   const int r = (int)(row % kRowTile);
@@ -86,6 +95,7 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
       }
     }
   }
+  }
 }
 
 // ------------------------------------------------------------- pq2_0 scales
@@ -93,8 +103,7 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
 // [tile][sc][row]; zero for padding rows.
 __global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows, int64_t nsc,
                                   int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
+  TQ_FOR_ITEMS(i, n) {
   const int r = (int)(i & 63);
   const int64_t rest = i >> 6;
   const int64_t sc = rest % nsc;
@@ -107,14 +116,14 @@ __global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __r
     v = (uint32_t)(b0[0] | (b0[1] << 8)) | ((uint32_t)(b1[0] | (b1[1] << 8)) << 16);
   }
   dst[i] = v;
+  }
 }
 
 // ------------------------------------------------------------- ptq1_0 scales
 // fp16 scale of (row, group) into [tile][g8][row][8]; zero for padding.
 __global__ void repack_scales(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows, int64_t G,
                               int64_t G8, int block_bytes, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
+  TQ_FOR_ITEMS(i, n) {
   const int gi = (int)(i & 7);
   const int r = (int)((i >> 3) & 63);
   const int64_t rest = i >> 9;
@@ -128,6 +137,7 @@ __global__ void repack_scales(const uint8_t* __restrict__ src, uint16_t* __restr
     h = (uint16_t)(blk[0] | (blk[1] << 8));
   }
   dst[i] = h;
+  }
 }
 
 // --------------------------------------------------------------- ptq1_0 codes
@@ -145,8 +155,7 @@ __device__ __forceinline__ int64_t ptq1_src_byte(int D, int bi, int64_t sb, int6
 
 __global__ void repack_ptq1_codes(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows, int64_t G,
                                   int64_t G8, int64_t ndw) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= ndw) return;
+  TQ_FOR_ITEMS(i, ndw) {
   const int c = (int)(i & 3);
   const int r = (int)((i >> 2) & 63);
   const int64_t rest = i >> 8;
@@ -166,12 +175,12 @@ __global__ void repack_ptq1_codes(const uint8_t* __restrict__ src, uint32_t* __r
     }
   }
   dst[i] = out;
+  }
 }
 
 __global__ void unrepack_ptq1_codes(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                     uint8_t* __restrict__ dst, int64_t rows, int64_t G, int64_t G8) {
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= rows * G) return;
+  TQ_FOR_ITEMS(b, rows * G) {
   const int64_t row = b / G, g = b % G;
   const int64_t tile = row / kRowTile;
   const int r = (int)(row % kRowTile);
@@ -194,6 +203,7 @@ __global__ void unrepack_ptq1_codes(const uint32_t* __restrict__ codes, const ui
     const int L = D / 4, c = D % 4;
     const int64_t dw = (((tile * G8 + sb) * kPtqLoads + L) * 64 + r) * 4 + c;
     out[2 + byte] = base[dw * 4 + bi];
+  }
   }
 }
 

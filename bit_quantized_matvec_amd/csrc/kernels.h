@@ -34,6 +34,9 @@ __host__ __device__ inline double* ws_partials(uint8_t* ws, int64_t tile) {
 }
 inline int64_t workspace_bytes(const Dims& d) { return d.ntiles * kWsTileBytes; }
 
+// Zero `bytes` bytes at p (16-byte aligned) with a kernel (graph-capturable).
+hipError_t launch_clear(void* p, int64_t bytes, hipStream_t s);
+
 hipError_t launch_quantize_q8k(const float* x, int64_t nblocks, int8_t* q, float* d, int16_t* bsums, hipStream_t s);
 
 hipError_t launch_repack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, int32_t* bad_flag, hipStream_t s);
@@ -81,7 +84,7 @@ hipError_t launch_gemv_ptq1(const uint8_t* w, const Dims& dm, const int8_t* q, c
 int ptq1_token_block(const Dims& dm, int64_t tokens);
 hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                             const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
-// The same on int8 MFMA: 32 tokens x 128 rows per workgroup.
+// The same on int8 MFMA: 16 tokens x one 64-row tile per workgroup.
 hipError_t launch_gemm_ptq1_mfma(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                                  const int16_t* bsums, float* y, int32_t* idots, hipStream_t s);
 // y[tokens][rows] or idots [tokens][rows][G].

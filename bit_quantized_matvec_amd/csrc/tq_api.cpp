@@ -14,7 +14,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int64_t kMaxCols = int64_t(1) << 20;
 constexpr int64_t kMaxWeights = int64_t(1) << 36;
 constexpr int64_t kMaxTokens = int64_t(1) << 20;
-constexpr int64_t kMaxPtq1Cols = 32768;  // the ptq1_0 activation table (1792 B per 1024 cols) and a 4 KiB copy of q stay within 64 KiB of LDS
+constexpr int64_t kMaxPtq1Cols = 32768;  // the ptq1_0 tables of one workgroup (1792 B per 1024 cols and token) stay within its LDS budget
 
 bool fmt_ok(int f) { return f == TQ_FMT_PQ2_0 || f == TQ_FMT_PTQ1_0; }
 
@@ -101,6 +101,14 @@ int tq_quantize_q8k(const float* x, int64_t tokens, int64_t cols, int8_t* q, flo
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens) {
   if (shape_status(fmt, rows, cols, tokens) != TQ_OK) return 0;
   return tq::workspace_bytes(tq::dims(rows, cols));
+}
+
+int tq_workspace_clear(void* workspace, int64_t bytes, void* stream) {
+  if (bytes < 0) return TQ_ERR_SHAPE;
+  if (bytes == 0) return TQ_OK;
+  if (!workspace) return TQ_ERR_NULL;
+  if (!aligned(workspace, 16)) return TQ_ERR_ALIGN;
+  return hip_status(tq::launch_clear(workspace, bytes, as_stream(stream)));
 }
 
 int tq_gemv(int fmt, const void* w, int64_t rows, int64_t cols, const int8_t* q, const float* d, const int16_t* bsums,

@@ -106,20 +106,37 @@ int tq_unrepack(int fmt, const void *src_repacked, void *dst, int64_t rows, int6
  * d == 0 gives q = 0 and bsums = 0.  Inputs must be finite. */
 int tq_quantize_q8k(const float *x, int64_t tokens, int64_t cols, int8_t *q, float *d, int16_t *bsums, void *stream);
 
-/* Bytes of the optional workspace of tq_gemv / tq_gemm for this shape.  The
- * workspace lets a product split its columns over several workgroups per
- * 64-row tile (fp64 partial sums plus per-tile arrival counters), which keeps
- * all compute units busy when the row count is small and balances the load
- * when it is large.  Contract: device memory of at least this size, 16-byte
- * aligned, zero-filled once before its first use.  It holds one block of
- * 16400 bytes per 64-row tile, laid out alike for every shape, format and
- * entry point: the tile's 32-bit arrival counter, which every call returns to
- * zero, then fp64 partial sums that are always written before they are read
- * and keep whatever the last call left.  So it can be reused by later calls of
- * any shape, format and token count whose tile count it covers (also inside a
- * captured graph) without clearing.  Calls that run at the same time must not
- * share one.  Returns 0 for an invalid shape. */
+/* Bytes of the optional workspace of tq_gemv / tq_gemv_f32 / tq_gemv_f32_batch
+ * for this shape (tq_gemm uses it only for a single token).  The workspace lets a product
+ * split its columns over several workgroups per 64-row tile (fp64 partial
+ * sums plus per-tile arrival counters), which keeps all compute units busy
+ * when the row count is small.  It holds one block of 16400 bytes per 64-row
+ * tile, laid out alike for every shape, format and entry point: the tile's
+ * 32-bit arrival counter, then fp64 partial sums that are always written
+ * before they are read.
+ *
+ * Contract: device memory of at least this size, 16-byte aligned, whose
+ * counters are zero when a call starts.  Zero it once before first use
+ * (tq_workspace_clear, or any zero fill).  Every call that completes returns
+ * the counters it used to zero, so the workspace can then be reused by later
+ * calls of any shape, format and token count whose tile count it covers (also
+ * inside a captured graph) without clearing.  Calls that run at the same time
+ * must not share one.
+ *
+ * What breaks the contract: a counter that is not zero at entry (a workspace
+ * never cleared, or two overlapping calls on one workspace) makes a tile's
+ * reduction run early or never: its y entries are then wrong or left
+ * unwritten, with no error reported.  A call cannot be interrupted part-way
+ * except by a fault that ends the HIP context.  Recover by calling
+ * tq_workspace_clear on the workspace (stream-ordered) before the next call.
+ * Returns 0 for an invalid shape. */
 int64_t tq_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t tokens);
+
+/* Zero `bytes` bytes of a workspace (device memory, 16-byte aligned) with a
+ * kernel on `stream`.  It records no memset, so it may be captured in a
+ * graph.  Returns TQ_OK (nothing launched for bytes == 0), TQ_ERR_NULL,
+ * TQ_ERR_ALIGN, TQ_ERR_SHAPE (bytes < 0) or TQ_ERR_HIP. */
+int tq_workspace_clear(void *workspace, int64_t bytes, void *stream);
 
 /* Matrix-vector product, one token (page 1, "the trick with 4 and 16" and
  * "did it reach the wall?"):

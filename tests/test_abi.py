@@ -99,6 +99,10 @@ def test_validation_errors_touch_nothing(tq):
     assert L.tq_unrepack(9, good, good, 64, 256, None) == tq.ERR_FORMAT
     assert L.tq_gemv(1, good, 64, 256, good, good, None, good, P(0x100008), None) == tq.ERR_ALIGN  # workspace
     assert L.tq_workspace_bytes(1, 64, 200, 1) == 0 and L.tq_workspace_bytes(1, 640, 8192, 1) > 0
+    assert L.tq_workspace_clear(None, 64, None) == tq.ERR_NULL
+    assert L.tq_workspace_clear(P(0x100008), 64, None) == tq.ERR_ALIGN
+    assert L.tq_workspace_clear(good, -1, None) == tq.ERR_SHAPE
+    assert L.tq_workspace_clear(None, 0, None) == tq.OK  # nothing to clear, nothing launched
     assert L.tq_last_hip_error() == 0
 
 

@@ -621,11 +621,14 @@ def test_gemm_long_rows(tq, orc, R, K, T):
 
 
 @pytest.mark.parametrize("R,K,T", [(3, 32768, 3), (70, 16384, 5), (64, 8192, 7), (64, 8192, 9), (3, 32768, 16),
-                                   (130, 1280, 8), (65, 3328, 31), (1, 256, 33)])
+                                   (130, 1280, 8), (65, 3328, 31), (1, 256, 33),
+                                   # 2-token blocks whose tables take 70 and 77 KiB of LDS (above 64 KiB)
+                                   (64, 20480, 3), (64, 22528, 3)])
 def test_gemm_ptq1_token_blocks(tq, orc, R, K, T):
     """ptq1_0 prompt products: below 8 tokens the vector-unit kernel, whose
     token-block tables fill the LDS budget (one token per block at the column
-    limit, two at 16384 columns, a padded last block at 8192); from 8 tokens
+    limit, two at 16384 columns, a padded last block at 8192, two tokens with
+    more than 64 KiB of tables at 20480 and 22528 columns); from 8 tokens
     the MFMA kernel (16 tokens per workgroup: ragged rows, ragged last token
     block, superblocks of fewer than 8 groups, the column limit)."""
     g = TI.rng(77, 17, R, K)
