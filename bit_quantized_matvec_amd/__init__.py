@@ -39,6 +39,7 @@ _SIGS = {
     "tq_gemv": ([_i32, _p, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_gemv_f32": ([_i32, _p, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_gemv_f32_batch": ([_i32, _i32, _p, _p, _i64, _p, _p, _p, _p], _i32),
+    "tq_gemv_f32_scratch": ([_i32, _p, _i64, _i64, _p, _p, _p], _i32),
     "tq_gemm": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p], _i32),
     "tq_group_dots": ([_i32, _p, _i64, _i64, _i64, _p, _p, _p, _p], _i32),
     "tq_status_str": ([_i32], ctypes.c_char_p),
@@ -243,6 +244,21 @@ def gemv_f32(fmt, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, out=No
     _need(out, torch.float32, "out", rows, device=w.device)
     _need_ws(ws, fmt, rows, cols, 1, w.device)
     _check(_lib.tq_gemv_f32(_fmt(fmt), _ptr(w), rows, cols, _ptr(x), _ptr(out), _ptr(ws), _stream()), "tq_gemv_f32")
+    return out
+
+
+def gemv_f32_scratch(fmt, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, out=None) -> torch.Tensor:
+    """gemv_f32 with the column split's workspace in the library's static
+    device scratch (no workspace argument, nothing allocated by the call
+    itself when `out` is given).  Calls that overlap on one GPU race."""
+    _shape(fmt, rows, cols, 1, "tq_gemv_f32_scratch")
+    _need_w(w, fmt, rows, cols)
+    _need(x, torch.float32, "x", cols, device=w.device)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=w.device)
+    _need(out, torch.float32, "out", rows, device=w.device)
+    _check(_lib.tq_gemv_f32_scratch(_fmt(fmt), _ptr(w), rows, cols, _ptr(x), _ptr(out), _stream()),
+           "tq_gemv_f32_scratch")
     return out
 
 

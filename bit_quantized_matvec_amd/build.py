@@ -22,7 +22,7 @@ PROBE_LIB = os.path.join(HERE, "libtq_probe.so")
 PROBE_SOURCES = ["hbm_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["tq_api.cpp", "k_workspace.hip", "k_quant.hip", "k_repack.hip", "k_gemv_pq2.hip", "k_gemm_pq2.hip", "k_gemv_ptq1.hip", "k_gemm_ptq1.hip"]
+SOURCES = ["tq_api.cpp", "k_workspace.hip", "scratch.hip", "k_quant.hip", "k_repack.hip", "k_gemv_pq2.hip", "k_gemm_pq2.hip", "k_gemv_ptq1.hip", "k_gemm_ptq1.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -71,6 +71,10 @@ struct GemvBatch {
 };
 // `dm` describes the whole batch: ntiles = tile0[n], cols the common count
 hipError_t launch_gemv_pq2_fused_batch(const GemvBatch& b, const Dims& dm, void* workspace, hipStream_t s);
+// The library's static device scratch (scratch.hip): its size, and this
+// device's address (looked up and zero-filled on `s` at the first call).
+int64_t scratch_bytes();
+hipError_t scratch_ptr(hipStream_t s, void** out);
 hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* x, float* y, void* workspace,
                                  hipStream_t s);
 GemvPlan plan_gemv_ptq1(const Dims& dm, bool have_workspace);

@@ -134,6 +134,22 @@ int tq_gemv_f32(int fmt, const void* w, int64_t rows, int64_t cols, const float*
   return hip_status(tq::launch_gemv_pq2_fused(static_cast<const uint8_t*>(w), dm, x, y, workspace, as_stream(stream)));
 }
 
+int tq_gemv_f32_scratch(int fmt, const void* w, int64_t rows, int64_t cols, const float* x, float* y, void* stream) {
+  const int st = shape_status(fmt, rows, cols, 1);
+  if (st != TQ_OK) return st;
+  const tq::Dims dm = tq::dims(rows, cols);
+  if (fmt != TQ_FMT_PQ2_0 || !tq::gemv_pq2_fused_fits(dm, true)) return TQ_ERR_UNSUPPORTED;
+  // the split's workspace must fit the static scratch (always, for the current plan)
+  const tq::GemvPlan p = tq::plan_gemv_pq2(dm, true);
+  if (p.slices > 1 && tq::workspace_bytes(dm) > tq::scratch_bytes()) return TQ_ERR_UNSUPPORTED;
+  if (!w || !x || !y) return TQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return TQ_ERR_ALIGN;
+  void* ws = nullptr;
+  const hipError_t e = tq::scratch_ptr(as_stream(stream), &ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(tq::launch_gemv_pq2_fused(static_cast<const uint8_t*>(w), dm, x, y, ws, as_stream(stream)));
+}
+
 int tq_gemv_f32_batch(int fmt, int n, const void* const* w, const int64_t* rows, int64_t cols, const float* const* x,
                       float* const* y, void* workspace, void* stream) {
   if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;

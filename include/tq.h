@@ -168,6 +168,22 @@ int tq_gemv(int fmt, const void *w, int64_t rows, int64_t cols, const int8_t *q,
 int tq_gemv_f32(int fmt, const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *workspace,
                 void *stream);
 
+/* tq_gemv_f32 without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the column split's workspace is the library's own
+ * static device scratch (6,297,600 bytes per GPU, held until the process
+ * ends), so the call allocates nothing.  The result is bit-identical to
+ * tq_gemv_f32 with a zeroed workspace of tq_workspace_bytes.  The scratch is
+ * looked up and zero-filled (with a kernel, on `stream`) at the first call on
+ * a device.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents (the tile counters are back at zero after each
+ * call): calls that overlap on one GPU (concurrent streams, or threads) race
+ * and may return wrong or unwritten outputs.  Shapes and errors as for
+ * tq_gemv_f32; a shape whose split would need more than the scratch returns
+ * TQ_ERR_UNSUPPORTED (none does: the split is used only below 384 row tiles,
+ * which the scratch covers). */
+int tq_gemv_f32_scratch(int fmt, const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *stream);
+
 /* Several independent tq_gemv_f32 products with the same column count in one
  * launch (page 1, "what's running": a decode step runs one product after
  * another for every projection of every layer; products that do not depend
