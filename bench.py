@@ -550,6 +550,15 @@ def _read_csvs(d, suffix):
     return rows
 
 
+def _dims(r):
+    """(grid work-items, workgroup size) of a counter-collection or kernel-trace row."""
+    def total(base):
+        if base in r and r[base] not in (None, ""):
+            return int(r[base])
+        return int(r[base + "_X"]) * int(r.get(base + "_Y") or 1) * int(r.get(base + "_Z") or 1)
+    return total("Grid_Size"), total("Workgroup_Size")
+
+
 def short_name(name: str) -> str:
     if name.startswith("void "):
         name = name[5:]
@@ -558,14 +567,27 @@ def short_name(name: str) -> str:
     return name[:cut] if cut > 0 else name
 
 
+NUM_XCD = 8  # rocprofv3 sums GRBM_GUI_ACTIVE over the eight XCDs
+
+
 def summarize(counter_dir, trace_dir=None):
     """Median counter value per (kernel, grid) from rocprofv3 counter-collection
     CSVs; byte counters scaled by what they read for the 1 GiB device copy;
-    derived MFMA / VALU / LDS figures; durations from a kernel-trace CSV."""
+    durations and back-to-back launch periods from a kernel-trace CSV; derived
+    figures:
+      mfma_ops        = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 (2 ops per int8 MAC)
+      mfma_util       = mfma_ops / (trace duration x dense int8 peak)
+      gui_cycles      = GRBM_GUI_ACTIVE / 8 (one XCD's busy cycles)
+      valu_busy       = SQ_ACTIVE_INST_VALU x 4 / (SIMDs x gui_cycles): the
+                        share of SIMD cycles issuing VALU (the counter is in
+                        quad-cycles, summed over waves)
+      mfma_busy       = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x gui_cycles)"""
     rows = _read_csvs(counter_dir, "counter_collection.csv") if counter_dir else []
     vals = {}
+    lds = {}
     for r in rows:
-        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]), int(r["LDS_Block_Size"]))
+        key = (short_name(r["Kernel_Name"]),) + _dims(r)
+        lds[key] = int(r["LDS_Block_Size"])
         vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     med = {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
     # calibration: the 1 GiB copy reads and writes exactly 2^30 bytes
@@ -575,38 +597,53 @@ def summarize(counter_dir, trace_dir=None):
         got = [cs[c] for cs in copy if c in cs]
         if got:
             scale[c] = (1 << 30) / (max(got) * 1024.0)
-    durations = {}
+    durations, periods = {}, {}
     if trace_dir:
+        trace = []
         for r in _read_csvs(trace_dir, "kernel_trace.csv"):
-            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]), int(r["LDS_Block_Size"]))
-            durations.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            key = (short_name(r["Kernel_Name"]),) + _dims(r)
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            trace.append((t0, t1, key))
+            durations.setdefault(key, []).append((t1 - t0) * 1e-3)
+        trace.sort()
+        # start-to-start interval of consecutive launches of one kernel with
+        # nothing between them (a graph replay): the per-launch time that a
+        # replay timed with events measures
+        for (s0, _e0, k0), (s1, _e1, k1) in zip(trace, trace[1:]):
+            if k0 == k1:
+                periods.setdefault(k0, []).append((s1 - s0) * 1e-3)
     out = {}
     for key in sorted(set(med) | set(durations), key=lambda k: (k[0], k[1])):
         fam = kernel_family(key[0])
         if fam is None and "copyBuffer" not in key[0] and "read_kernel" not in key[0]:
             continue
         cs = med.get(key, {})
-        e = {"kernel": key[0], "grid": key[1], "block": key[2], "lds": key[3], "family": fam}
+        e = {"kernel": key[0], "grid": key[1], "block": key[2], "lds": lds.get(key), "family": fam}
         for c, v in cs.items():
             e[c] = v
         if "FETCH_SIZE" in cs and "FETCH_SIZE" in scale:
             e["fetch_bytes"] = cs["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
         if "WRITE_SIZE" in cs and "WRITE_SIZE" in scale:
             e["write_bytes"] = cs["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
-        gui = cs.get("GRBM_GUI_ACTIVE")
-        if gui:
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
-                # share of the CUs' matrix-core cycles that were busy while the GPU was active
-                e["mfma_busy_frac"] = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * NUM_CU * 4)
-            if "SQ_ACTIVE_INST_VALU" in cs:
-                e["valu_active_frac"] = cs["SQ_ACTIVE_INST_VALU"] / (gui * NUM_CU * 4)
-            if "SQ_BUSY_CYCLES" in cs:
-                e["sq_busy_frac"] = cs["SQ_BUSY_CYCLES"] / gui
         if key in durations:
             ds = durations[key]
             e["trace_launches"] = len(ds)
             e["trace_avg_us"] = sum(ds) / len(ds)
             e["trace_median_us"] = statistics.median(ds)
+        if len(periods.get(key, [])) >= 5:
+            e["trace_period_us"] = statistics.median(periods[key])
+        if "SQ_INSTS_VALU_MFMA_MOPS_I8" in cs:
+            e["mfma_ops"] = cs["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
+            if "trace_avg_us" in e:
+                e["mfma_util"] = e["mfma_ops"] / (e["trace_avg_us"] * 1e-6 * INT8_MFMA_PEAK_TOPS * 1e12)
+        gui = cs.get("GRBM_GUI_ACTIVE")
+        if gui:
+            cyc = gui / NUM_XCD
+            e["gui_cycles"] = cyc
+            if "SQ_ACTIVE_INST_VALU" in cs:
+                e["valu_busy"] = cs["SQ_ACTIVE_INST_VALU"] * 4 / (NUM_CU * 4 * cyc)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+                e["mfma_busy"] = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_CU * 4 * cyc)
         if fam:
             e["source_sha256"] = source_sha256(KERNEL_SOURCES[fam])
         out[f"{key[0]} grid={key[1]} block={key[2]}"] = e
@@ -614,19 +651,20 @@ def summarize(counter_dir, trace_dir=None):
 
 
 def print_summary(s):
-    cols = ["fetch_bytes", "write_bytes", "SQ_INSTS_VALU_MFMA_MOPS_I8", "mfma_busy_frac", "valu_active_frac",
-            "SQ_INSTS_VALU", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "VALUBusy", "trace_avg_us"]
+    cols = ["trace_launches", "trace_avg_us", "trace_period_us", "fetch_bytes", "write_bytes", "mfma_ops", "mfma_util",
+            "mfma_busy", "valu_busy", "VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS",
+            "SQ_LDS_BANK_CONFLICT", "gui_cycles"]
     present = [c for c in cols if any(c in e for e in s["kernels"].values())]
     print("byte-counter scale (bytes per KiB read):", {k: round(v, 6) for k, v in s["scale"].items()})
     print()
-    print("| kernel | grid / block | " + " | ".join(present) + " |")
+    print("| kernel | grid / block / LDS | " + " | ".join(present) + " |")
     print("|---|---|" + "---|" * len(present))
     for e in s["kernels"].values():
         cells = []
         for c in present:
             v = e.get(c)
             cells.append("" if v is None else (f"{v:.4g}" if isinstance(v, float) else str(v)))
-        print(f"| {e['kernel']} | {e['grid']} / {e['block']} | " + " | ".join(cells) + " |")
+        print(f"| {e['kernel']} | {e['grid']} / {e['block']} / {e['lds']} | " + " | ".join(cells) + " |")
 
 
 # ----------------------------------------------------------------- CPU oracle
@@ -728,8 +766,9 @@ def main():
     ceil = ceiling_bench(torch, dec["Ws"], min(K, 1000), trials)
     del dec["Ws"]
     counters = recorded_counters()
+    # the timed kernel: gemv_pq2_kernel<RING, IDOTS=false, NT, LDSQ, FX=true, XB> on 512 workgroups of 256
     fused = {k: v for k, v in counters.items() if v.get("family") == "gemv_pq2_kernel" and v.get("grid") == 131072
-             and v.get("lds", 0) > 16384}
+             and "false, true, true, true," in v.get("kernel", "")}
     traffic = None
     for v in fused.values():
         if "fetch_bytes" in v and "write_bytes" in v:
@@ -783,9 +822,8 @@ def main():
         extra["quantize_8192"] = rounded(quantize_bench(torch, tq, 200, trials), 3)
         extra["tiny_256x1024"] = rounded(tiny_bench(torch, tq, 1000, trials), 3)
     if counters:
-        extra["counters"] = {k: rounded({c: v[c] for c in ("fetch_bytes", "write_bytes", "mfma_busy_frac",
-                                                          "valu_active_frac", "SQ_INSTS_VALU_MFMA_MOPS_I8",
-                                                          "trace_avg_us") if c in v}, 4)
+        extra["counters"] = {k: rounded({c: v[c] for c in ("fetch_bytes", "write_bytes", "mfma_util", "mfma_busy",
+                                                          "valu_busy", "trace_avg_us", "trace_period_us") if c in v}, 4)
                              for k, v in counters.items()}
     out["extra"] = extra
     if not args.no_cpu:
