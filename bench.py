@@ -56,6 +56,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS = 2 x MAC/s)
 MALL_BYTES = 256 << 20
 NUM_CU = 256
+PEAK_SCLK_GHZ = 2.4  # MI355X peak shader clock
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc")
 
@@ -581,7 +582,12 @@ def summarize(counter_dir, trace_dir=None):
       valu_busy       = SQ_ACTIVE_INST_VALU x 4 / (SIMDs x gui_cycles): the
                         share of SIMD cycles issuing VALU (the counter is in
                         quad-cycles, summed over waves)
-      mfma_busy       = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x gui_cycles)"""
+      mfma_busy       = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x gui_cycles)
+      valu_issue_us   = SQ_ACTIVE_INST_VALU x 4 / SIMDs / 2.4 GHz: one SIMD's
+                        VALU issue time at the peak clock
+      valu_frac_trace = valu_issue_us / trace_avg_us (a lower bound of the
+                        SIMDs' VALU-busy share over the kernel's own run:
+                        GRBM_GUI_ACTIVE also counts cycles around it)"""
     rows = _read_csvs(counter_dir, "counter_collection.csv") if counter_dir else []
     vals = {}
     lds = {}
@@ -636,6 +642,10 @@ def summarize(counter_dir, trace_dir=None):
             e["mfma_ops"] = cs["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
             if "trace_avg_us" in e:
                 e["mfma_util"] = e["mfma_ops"] / (e["trace_avg_us"] * 1e-6 * INT8_MFMA_PEAK_TOPS * 1e12)
+        if "SQ_ACTIVE_INST_VALU" in cs:
+            e["valu_issue_us"] = cs["SQ_ACTIVE_INST_VALU"] * 4 / (NUM_CU * 4) / (PEAK_SCLK_GHZ * 1e3)
+            if "trace_avg_us" in e:
+                e["valu_frac_trace"] = e["valu_issue_us"] / e["trace_avg_us"]
         gui = cs.get("GRBM_GUI_ACTIVE")
         if gui:
             cyc = gui / NUM_XCD
@@ -652,7 +662,7 @@ def summarize(counter_dir, trace_dir=None):
 
 def print_summary(s):
     cols = ["trace_launches", "trace_avg_us", "trace_period_us", "fetch_bytes", "write_bytes", "mfma_ops", "mfma_util",
-            "mfma_busy", "valu_busy", "VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS",
+            "mfma_busy", "valu_issue_us", "valu_frac_trace", "valu_busy", "VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS",
             "SQ_LDS_BANK_CONFLICT", "gui_cycles"]
     present = [c for c in cols if any(c in e for e in s["kernels"].values())]
     print("byte-counter scale (bytes per KiB read):", {k: round(v, 6) for k, v in s["scale"].items()})
@@ -823,7 +833,8 @@ def main():
         extra["tiny_256x1024"] = rounded(tiny_bench(torch, tq, 1000, trials), 3)
     if counters:
         extra["counters"] = {k: rounded({c: v[c] for c in ("fetch_bytes", "write_bytes", "mfma_util", "mfma_busy",
-                                                          "valu_busy", "trace_avg_us", "trace_period_us") if c in v}, 4)
+                                                          "valu_frac_trace", "trace_avg_us", "trace_period_us")
+                                         if c in v}, 4)
                              for k, v in counters.items()}
     out["extra"] = extra
     if not args.no_cpu:
