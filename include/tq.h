@@ -74,7 +74,9 @@ enum {
  * the selector should reject).  Returns TQ_OK or TQ_ERR_SHAPE/TQ_ERR_FORMAT. */
 int tq_check_shape(int fmt, int64_t rows, int64_t cols, int64_t tokens);
 
-/* Bytes of the canonical matrix: 34 (pq2_0) or 28 (ptq1_0) per 128 weights.
+/* Bytes of the canonical matrix (ciot README, format notes: a pq2_0 block is
+ * an fp16 scale and 32 bytes of 2-bit codes, a ptq1_0 block an fp16 scale and
+ * 26 bytes of base-3 codes): 34 (pq2_0) or 28 (ptq1_0) per 128 weights.
  * Returns 0 for an invalid format or shape. */
 int64_t tq_canonical_bytes(int fmt, int64_t rows, int64_t cols);
 
@@ -217,9 +219,10 @@ int tq_gemv_f32_batch(int fmt, int n, const void *const *w, const int64_t *rows,
 int tq_gemm(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q, const float *d,
             const int16_t *bsums, float *y, void *workspace, void *stream);
 
-/* Test export: the exact integer group dots I[t][r][g] (int32,
- * [tokens][rows][cols/128]) computed by the same kernels as tq_gemv
- * (tokens == 1) and tq_gemm (tokens > 1). */
+/* Test export: the exact integer group dots I[t][r][g] (page 1, "the trick
+ * with 4 and 16": the integer dot of one 128-weight group with its int8
+ * activations, before any scale) (int32, [tokens][rows][cols/128]), computed
+ * by the same kernels as tq_gemv (tokens == 1) and tq_gemm (tokens > 1). */
 int tq_group_dots(int fmt, const void *w, int64_t rows, int64_t cols, int64_t tokens, const int8_t *q,
                   const int16_t *bsums, int32_t *idots, void *stream);
 
