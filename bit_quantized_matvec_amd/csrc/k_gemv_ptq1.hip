@@ -8,7 +8,8 @@
 // How (gfx950):
 //   * one lane = one row, a workgroup = a 64-row tile, waves split the
 //     8-group superblocks; 13 fully coalesced dwordx4 loads per row and
-//     superblock (1.75 bits per weight, bytes only reordered by the repack);
+//     superblock (1.75 bits per weight, bytes only reordered by the repack),
+//     requested in two halves;
 //   * the four bytes of a code dword are spread over the four 16-bit lanes of
 //     a 64-bit register, so one 64-bit shift-and-add (x + 2x) advances all
 //     four at once without carries between them, and one v_perm_b32 gathers
@@ -220,8 +221,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = 0.0;
     // Loads 0..11 hold the 48 full dwords (3 loads per group pair), load 12
-    // the four leftover dwords.  All 13 and the scales are requested at once,
-    // in the order they are used; group pair gp waits for its own three.
+    // the four leftover dwords.  Group pairs 0 and 1 (with the leftover
+    // dwords and the scales) are requested first, pairs 2 and 3 once pair 0
+    // is done: with every wave of the chip starting its superblock at once,
+    // half the requests in flight stream faster than the whole superblock's
+    // (measured on 32768 x 8192: 16.3 us -> 15.7-16.0 us).
     const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
     uint4 cw[13];
 #pragma unroll
@@ -229,11 +233,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
     cw[12] = cp[12 * 64];
     const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
 #pragma unroll
-    for (int k = 3; k < 12; ++k) cw[k] = cp[k * 64];
+    for (int k = 3; k < 6; ++k) cw[k] = cp[k * 64];
     const uint4 left = cw[12];
     const uint32_t* tb = table + (size_t)(sb - wg0) * kTableDwords * NT;
 #pragma unroll
     for (int gp = 0; gp < 4; ++gp) {
+      if (gp == 1) {
+#pragma unroll
+        for (int k = 6; k < 12; ++k) cw[k] = cp[k * 64];
+      }
       const uint4* cur = cw + 3 * gp;
       const uint32_t dws[13] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z,
                                 cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
