@@ -115,7 +115,7 @@ struct GemmShape {
 // Every operand streams through a ring of RD superchunks in registers.
 template <int NT, int RD, int MRB, bool IDOTS>
 __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
-    const v4u* __restrict__ codes, const uint32_t* __restrict__ scales, const int8_t* __restrict__ q,
+    const v4u* __restrict__ codes, const int8_t* __restrict__ q,
     const float* __restrict__ dx, float* __restrict__ y, int32_t* __restrict__ idots, int rows, int nsc, int tokens,
     int spw, GemmShape gs) {
   constexpr int kAcc = MRB * NT * 4;  // fp64 sums per lane
@@ -146,21 +146,24 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
   const int ntl = min(2, (rows + 63) / 64 - tile0);  // tiles of this row range
   const int ntok = min(16 * NT, tokens - tok0);
   const buf_t none = make_buf(codes, 0);
-  const buf_t a_buf = make_buf(codes + (size_t)tile0 * nsc * 256, ntl * nsc * 4096);
-  const buf_t s_buf = make_buf(scales + (size_t)tile0 * nsc * 64, ntl * nsc * 256);
+  // units (tile, sc) of kPq2UnitBytes: codes, then the scale pairs
+  constexpr int kUnit = (int)kPq2UnitBytes;
+  const uint8_t* units = reinterpret_cast<const uint8_t*>(codes) + (size_t)tile0 * nsc * kUnit;
+  const buf_t a_buf = make_buf(units, ntl * nsc * kUnit);
+  const buf_t s_buf = make_buf(units + kPq2ScaleOffset, ntl * nsc * kUnit - (int)kPq2ScaleOffset);
   const buf_t b_buf = make_buf(q + (size_t)tok0 * K, ntok * K);
   const buf_t x_buf = make_buf(dx + (size_t)tok0 * nsc, ntok * nsc * 4);
   // byte offsets: codes of row block i at superchunk sc are at a_off[i] +
-  // 4096 sc, lane (l16, qd) reading 16 bytes at (64 qd + l16) * 16; its
-  // scale pair at s_off[i] + 256 sc + 4 l16; token block nb's activations at
+  // kUnit sc, lane (l16, qd) reading 16 bytes at (64 qd + l16) * 16; its
+  // scale pair at s_off[i] + kUnit sc + 4 l16; token block nb's activations at
   // (16 nb + l16) K + 16 qd + 256 sc + 64 c; d_x of token `lane` at 4 (lane
   // nsc + sc), lanes past 16 NT out of range
   int a_off[MRB], s_off[MRB];
 #pragma unroll
   for (int i = 0; i < MRB; ++i) {
     const int b = b0 + i, tl = (b >> 2) - tile0, rbi = b & 3;
-    a_off[i] = (tl * nsc * 256 + 16 * rbi) * 16;
-    s_off[i] = (tl * nsc * 64 + 16 * rbi) * 4;
+    a_off[i] = tl * nsc * kUnit + 16 * rbi * 16;
+    s_off[i] = tl * nsc * kUnit + 16 * rbi * 4;
   }
   const int a_lane = (64 * qd + l16) * 16, s_lane = 4 * l16;
   const int x_lane = lane < 16 * NT ? 4 * lane * nsc : 0x7fffff00;
@@ -175,8 +178,8 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
     for (int i = 0; i < MRB; ++i) {
       const bool use = real && i < nrb;
-      ra[J][i] = load16_nt(use ? a_buf : none, a_lane, a_off[i] + 4096 * sc);
-      if (!IDOTS) rs[J][i] = load4(use ? s_buf : none, s_lane, s_off[i] + 256 * sc);
+      ra[J][i] = load16_nt(use ? a_buf : none, a_lane, a_off[i] + kUnit * sc);
+      if (!IDOTS) rs[J][i] = load4(use ? s_buf : none, s_lane, s_off[i] + kUnit * sc);
     }
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) {
@@ -328,12 +331,11 @@ hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const
   const dim3 grid((unsigned)((int64_t)gs.nrg * gs.ntg)), block(64 * nruns);
   const size_t lds = gemm_lds_bytes<NT, MRB>(nruns);
   const v4u* codes = reinterpret_cast<const v4u*>(w);
-  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
   if (idots)
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, true>), grid, block, lds, s, codes, scales, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, true>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   else
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, false>), grid, block, lds, s, codes, scales, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, false>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   return hipGetLastError();
 }

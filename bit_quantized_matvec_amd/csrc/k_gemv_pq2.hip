@@ -11,7 +11,8 @@
 //     columns; its waves split the slice into runs of 256-column superchunks;
 //   * per superchunk a lane issues four non-temporal dwordx4 loads (qd = 0..3),
 //     each a fully coalesced 1 KiB wave request (the codes are never reused),
-//     plus its row's scale pair, two superchunks ahead of their use;
+//     plus its row's scale pair from the 256 bytes that follow the codes in
+//     the same 4352-byte unit, two superchunks ahead of their use;
 //   * the activation bytes a lane needs are the same for every lane of the
 //     wave: the workgroup stages its slice of them in LDS once, and each
 //     superchunk's 256 bytes are read from there with broadcast 16-byte
@@ -116,8 +117,11 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   const int sc0 = min(wg1, wg0 + wave * spw);
   const int sc1 = min(wg1, sc0 + spw);
 
-  const uint4* cp = codes + (size_t)tile * nsc * 256 + lane;
-  const uint32_t* sp = scales + (size_t)tile * nsc * 64 + lane;
+  // unit (tile, sc): 272 uint4 (256 of codes, then the 16 holding the 64
+  // scale pairs); `scales` points at the first unit's scale pairs
+  constexpr int kUnitU4 = (int)(kPq2UnitBytes / 16), kUnitDw = (int)(kPq2UnitBytes / 4);
+  const uint4* cp = codes + (size_t)tile * nsc * kUnitU4 + lane;
+  const uint32_t* sp = scales + (size_t)tile * nsc * kUnitDw + lane;
   double acc = 0.0;
 
   // The activations were typically written by the previous kernel, so every
@@ -172,8 +176,8 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   {                                                                                                      \
     const bool real = (K) < n;                                                                           \
     const int scf = sc0 + max(min((K), n - 1), 0);                                                       \
-    const uint4* c0 = real ? cp + (size_t)scf * 256 : dummy_c;                                           \
-    const uint32_t* s0 = real ? sp + (size_t)scf * 64 : dummy_s;                                         \
+    const uint4* c0 = real ? cp + (size_t)scf * kUnitU4 : dummy_c;                                       \
+    const uint32_t* s0 = real ? sp + (size_t)scf * kUnitDw : dummy_s;                                    \
     _Pragma("unroll") for (int qd = 0; qd < 4; ++qd) rc[J][qd] = load_codes<NT>(c0 + (real ? qd * 64 : 0)); \
     rsc[J] = *s0;                                                                                        \
   }
@@ -342,7 +346,7 @@ hipError_t launch_gemv_pq2_plan(const uint8_t* w, const Dims& dm, const int8_t* 
   constexpr int kRing = 2;
   const int nsc = (int)dm.nsc;
   const uint4* codes = reinterpret_cast<const uint4*>(w);
-  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
+  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + kPq2ScaleOffset);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   // one slice's activations are staged in LDS when they fit (always with the
@@ -384,7 +388,7 @@ hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* 
   const size_t stage = (size_t)p.scw * (256 + 4);
   if (stage > kMaxStageBytes) return hipErrorInvalidValue;  // the caller checks gemv_pq2_fused_fits first
   const uint4* codes = reinterpret_cast<const uint4*>(w);
-  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + pq2_code_bytes(dm));
+  const uint32_t* scales = reinterpret_cast<const uint32_t*>(w + kPq2ScaleOffset);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   // quantization batch: the blocks one wave quantizes (no more than 8 at once)

@@ -27,7 +27,8 @@ inline unsigned grid_for(int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < (n); i += (int64_t)gridDim.x * kThreads)
 
 // ---------------------------------------------------------------- pq2_0 codes
-// Output dword index i -> (tile, sc, qd, row, c).  Its byte j, field s holds
+// Code dword index i -> (tile, sc, qd, row, c), stored in unit (tile, sc) at
+// dword (qd * 64 + row) * 4 + c.  Its byte j, field s holds
 // the weight of column 256 sc + 64 c + 16 qd + 4 s + j, i.e. (in group
 // g = 2 sc + c/2, position k = 64 (c&1) + 16 qd + 4 s + j) field j of
 // canonical byte 16 (c&1) + 4 qd + s.  So the output dword is the 4x4
@@ -39,7 +40,7 @@ __global__ void repack_pq2_codes(const uint8_t* __restrict__ src, uint32_t* __re
   const int c = (int)(i & 3);
   const int r = (int)((i >> 2) & 63);
   const int qd = (int)((i >> 8) & 3);
-  const int64_t rest = i >> 10;
+  const int64_t rest = i >> 10;  // the unit, tile * nsc + sc
   const int64_t sc = rest % nsc;
   const int64_t tile = rest / nsc;
   const int64_t row = tile * kRowTile + r;
@@ -62,13 +63,13 @@ __global__ void repack_pq2_codes(const uint8_t* __restrict__ src, uint32_t* __re
     }
     if (bad && bad_flag) *bad_flag = 1;
   }
-  dst[i] = out;
+  dst[rest * (kPq2UnitBytes / 4) + (i & 1023)] = out;
   }
 }
 
 // Inverse: one thread per canonical 34-byte block.
-__global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ scales,
-                                   uint8_t* __restrict__ dst, int64_t rows, int64_t nsc) {
+__global__ void unrepack_pq2_codes(const uint32_t* __restrict__ units, uint8_t* __restrict__ dst, int64_t rows,
+                                   int64_t nsc) {
   const int64_t G = nsc * 2;
   TQ_FOR_ITEMS(b, rows * G) {
   const int64_t row = b / G, g = b % G;
@@ -76,14 +77,15 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
   const int r = (int)(row % kRowTile);
   const int64_t sc = g >> 1;
   uint8_t* out = dst + b * 34;
-  const uint32_t pair = scales[(tile * nsc + sc) * 64 + r];
+  const uint32_t* unit = units + (tile * nsc + sc) * (kPq2UnitBytes / 4);
+  const uint32_t pair = unit[kPq2ScaleOffset / 4 + r];
   const uint32_t h = (g & 1) ? pair >> 16 : pair & 0xffffu;
   out[0] = (uint8_t)(h & 0xff);
   out[1] = (uint8_t)(h >> 8);
   for (int qd = 0; qd < 4; ++qd) {
     for (int cc = 0; cc < 2; ++cc) {
       const int c = 2 * (int)(g & 1) + cc;
-      const uint32_t dw = codes[(((tile * nsc + sc) * 4 + qd) * 64 + r) * 4 + c];
+      const uint32_t dw = unit[(qd * 64 + r) * 4 + c];
       for (int s = 0; s < 4; ++s) {
         uint32_t byte = 0;
         for (int j = 0; j < 4; ++j) {
@@ -99,8 +101,8 @@ __global__ void unrepack_pq2_codes(const uint32_t* __restrict__ codes, const uin
 }
 
 // ------------------------------------------------------------- pq2_0 scales
-// fp16 scales of groups 2 sc, 2 sc + 1 of a row into one dword of
-// [tile][sc][row]; zero for padding rows.
+// fp16 scales of groups 2 sc, 2 sc + 1 of a row into dword `row` of unit
+// (tile, sc)'s scale pairs; zero for padding rows.
 __global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t rows, int64_t nsc,
                                   int64_t n) {
   TQ_FOR_ITEMS(i, n) {
@@ -115,7 +117,7 @@ __global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __r
     const uint8_t* b1 = b0 + 34;
     v = (uint32_t)(b0[0] | (b0[1] << 8)) | ((uint32_t)(b1[0] | (b1[1] << 8)) << 16);
   }
-  dst[i] = v;
+  dst[rest * (kPq2UnitBytes / 4) + kPq2ScaleOffset / 4 + r] = v;
   }
 }
 
@@ -216,15 +218,15 @@ hipError_t launch_repack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ns = pq2_scale_bytes(dm) / 4;
-  hipLaunchKernelGGL(repack_pq2_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src,
-                     reinterpret_cast<uint32_t*>(dst + pq2_code_bytes(dm)), dm.rows, dm.nsc, ns);
+  hipLaunchKernelGGL(repack_pq2_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src, reinterpret_cast<uint32_t*>(dst),
+                     dm.rows, dm.nsc, ns);
   return hipGetLastError();
 }
 
 hipError_t launch_unrepack_pq2(const uint8_t* src, uint8_t* dst, const Dims& dm, hipStream_t s) {
   const int64_t nb = dm.rows * dm.G;
   hipLaunchKernelGGL(unrepack_pq2_codes, dim3(grid_for(nb)), dim3(kThreads), 0, s, reinterpret_cast<const uint32_t*>(src),
-                     reinterpret_cast<const uint32_t*>(src + pq2_code_bytes(dm)), dst, dm.rows, dm.nsc);
+                     dst, dm.rows, dm.nsc);
   return hipGetLastError();
 }
 

@@ -62,7 +62,14 @@ inline Dims dims(int64_t rows, int64_t cols) {
   return d;
 }
 
-// Byte sizes and offsets of the repacked buffers.
+// pq2_0 is stored as one unit per (row tile, superchunk), tile-major: the
+// unit's 4096 bytes of codes (uint4 [qd][row]) and then its 256 bytes of
+// scale pairs (uint32 [row]), so that a superchunk is one contiguous read.
+constexpr int64_t kPq2UnitBytes = 4352;
+constexpr int64_t kPq2ScaleOffset = 4096;  // bytes from a unit's start to its scale pairs
+
+// Byte sizes of the repacked buffers (pq2_0: the code and scale shares of
+// its units).
 inline int64_t pq2_code_bytes(const Dims& d) { return d.ntiles * d.nsc * 4 * 64 * 16; }
 inline int64_t ptq1_code_bytes(const Dims& d) { return d.ntiles * d.G8 * kPtqLoads * 64 * 16; }
 inline int64_t pq2_scale_bytes(const Dims& d) { return d.ntiles * d.nsc * 64 * 4; }

@@ -173,7 +173,7 @@ int tq_gemv_f32_batch(int fmt, int n, const void* const* w, const int64_t* rows,
     const tq::Dims dmm = tq::dims(rows[m], cols);
     const uint8_t* wb = static_cast<const uint8_t*>(w[m]);
     b.codes[m] = reinterpret_cast<const uint4*>(wb);
-    b.scales[m] = reinterpret_cast<const uint32_t*>(wb + tq::pq2_code_bytes(dmm));
+    b.scales[m] = reinterpret_cast<const uint32_t*>(wb + tq::kPq2ScaleOffset);
     b.x[m] = reinterpret_cast<const float4*>(x[m]);
     b.y[m] = y[m];
     b.rows[m] = (int)rows[m];
