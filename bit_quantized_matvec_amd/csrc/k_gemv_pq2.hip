@@ -159,10 +159,11 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   // codes and the scale pair of superchunk j + RD are fetched while j is
   // multiplied.  The prologue fills the ring, so the state at the loop
   // header is the steady state and the compiler's wait counts stay exact.
-  // Two slots (8 KiB in flight per wave) measured fastest: deeper rings put
+  // Two slots (8 KiB in flight per wave), or one for short runs on a full
+  // grid (fused_ring), measured fastest: deeper rings put
   // more requests in flight per CU than HBM serves better.
   constexpr int RD = RING;
-  static_assert(RD == 2, "the passes below are written out for two slots");
+  static_assert(RD == 1 || RD == 2, "the passes below are written out for one or two slots");
   const int n = sc1 - sc0;
   v4u rc[RD][4];
   uint32_t rsc[RD];
@@ -221,7 +222,7 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
     };
     load_batch(0);
     TQ_FETCH(0, 0)
-    TQ_FETCH(1, 1)
+    if constexpr (RD > 1) TQ_FETCH(1, 1)
     __builtin_amdgcn_sched_barrier(0);  // all of those loads issue before the first quantization
     quant_batch(0);
     for (int b0 = kXB * nw; b0 < nb; b0 += kXB * nw) {
@@ -242,7 +243,7 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
 #pragma unroll
     for (int i = 0; i < XB; ++i) v[i] = src[min((int)threadIdx.x + i * (int)blockDim.x, nd4 - 1)];
     TQ_FETCH(0, 0)
-    TQ_FETCH(1, 1)
+    if constexpr (RD > 1) TQ_FETCH(1, 1)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < XB; ++i) dst[min((int)threadIdx.x + i * (int)blockDim.x, nd4 - 1)] = v[i];
@@ -250,10 +251,11 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
     qa = stage;
   } else {
     TQ_FETCH(0, 0)
-    TQ_FETCH(1, 1)
+    if constexpr (RD > 1) TQ_FETCH(1, 1)
   }
   for (int base = 0; base < n; base += RD) {
-    TQ_STEP(0) TQ_STEP(1)
+    TQ_STEP(0)
+    if constexpr (RD > 1) TQ_STEP(1)
   }
 #undef TQ_STEP
 #undef TQ_FETCH
@@ -304,14 +306,14 @@ __global__ __launch_bounds__(64 * kMaxWaves, 2) void gemv_pq2_kernel(const uint4
 
 // Several independent fused products with the same column count in one
 // launch: workgroup x belongs to problem m with tile0[m] <= x < tile0[m + 1].
-template <int XB>
+template <int RING, int XB>
 __global__ __launch_bounds__(64 * kMaxWaves, 2) void gemv_pq2_batch_kernel(GemvBatch b, int nsc, int G8, int scw, int spw,
                                                                         uint8_t* __restrict__ ws) {
   const int x = blockIdx.x;
   int m = 0;
 #pragma unroll
   for (int k = 1; k < kMaxBatch; ++k) m += (k < b.n && x >= b.tile0[k]) ? 1 : 0;
-  gemv_pq2_body<2, false, true, true, true, XB>(b.codes[m], b.scales[m], nullptr, nullptr, b.x[m], b.y[m], nullptr,
+  gemv_pq2_body<RING, false, true, true, true, XB>(b.codes[m], b.scales[m], nullptr, nullptr, b.x[m], b.y[m], nullptr,
                                                 b.rows[m], nsc, G8, scw, spw, ws, x - b.tile0[m], x);
 }
 
@@ -381,9 +383,17 @@ bool gemv_pq2_fused_fits(const Dims& dm, bool have_workspace) {
   return (size_t)p.scw * (256 + 4) <= kMaxStageBytes;
 }
 
+// Ring slots of the fused kernels (measured on MI355X, fused product, 2 / 1
+// slots): 17408 x 5120 (544 workgroups, runs of 3) 10.10 / 9.60 us and
+// 5120 x 17408 (480, runs of 3) 10.31 / 9.51 us take one slot; 32768 x 8192
+// (512, runs of 8) 13.6 / 15.3 us, 7168 x 5120 (224) 6.49 / 6.72 us and
+// 5120 x 6144 (240, runs of 2) 5.56 / 5.80 us keep two.  With short runs and
+// at least two workgroups per compute unit, a second slot in flight only
+// adds to the burst of requests at the start.
+int fused_ring(const Dims& dm, const GemvPlan& p) { return dm.ntiles * p.slices >= 448 && p.spw <= 3 ? 1 : 2; }
+
 hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* x, float* y, void* workspace,
                                  hipStream_t s) {
-  constexpr int kRing = 2;
   const GemvPlan p = plan_gemv_pq2(dm, workspace != nullptr);
   const size_t stage = (size_t)p.scw * (256 + 4);
   if (stage > kMaxStageBytes) return hipErrorInvalidValue;  // the caller checks gemv_pq2_fused_fits first
@@ -393,13 +403,14 @@ hipError_t launch_gemv_pq2_fused(const uint8_t* w, const Dims& dm, const float* 
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   // quantization batch: the blocks one wave quantizes (no more than 8 at once)
   const int per_wave = (p.scw + p.waves - 1) / p.waves;
-#define TQ_LAUNCH(XB)                                                                                             \
-  hipLaunchKernelGGL((gemv_pq2_kernel<kRing, false, true, true, true, XB>), grid, block, (unsigned)stage, s, codes, \
-                     scales, nullptr, nullptr, reinterpret_cast<const float4*>(x), y, nullptr, (int)dm.rows,        \
+  const int ring = fused_ring(dm, p);
+#define TQ_LAUNCH(RG, XB)                                                                                       \
+  hipLaunchKernelGGL((gemv_pq2_kernel<RG, false, true, true, true, XB>), grid, block, (unsigned)stage, s, codes, \
+                     scales, nullptr, nullptr, reinterpret_cast<const float4*>(x), y, nullptr, (int)dm.rows,     \
                      (int)dm.nsc, (int)dm.G8, p.scw, p.spw, ws)
-  if (per_wave <= 2) TQ_LAUNCH(2);
-  else if (per_wave <= 4) TQ_LAUNCH(4);
-  else TQ_LAUNCH(8);
+  if (per_wave <= 2) { if (ring == 1) TQ_LAUNCH(1, 2); else TQ_LAUNCH(2, 2); }
+  else if (per_wave <= 4) { if (ring == 1) TQ_LAUNCH(1, 4); else TQ_LAUNCH(2, 4); }
+  else { if (ring == 1) TQ_LAUNCH(1, 8); else TQ_LAUNCH(2, 8); }
 #undef TQ_LAUNCH
   return hipGetLastError();
 }
@@ -411,12 +422,13 @@ hipError_t launch_gemv_pq2_fused_batch(const GemvBatch& b, const Dims& dm, void*
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   const int per_wave = (p.scw + p.waves - 1) / p.waves;
-#define TQ_LAUNCH(XB)                                                                                                 \
-  hipLaunchKernelGGL(gemv_pq2_batch_kernel<XB>, grid, block, (unsigned)stage, s, b, (int)dm.nsc, (int)dm.G8, p.scw, \
-                     p.spw, ws)
-  if (per_wave <= 2) TQ_LAUNCH(2);
-  else if (per_wave <= 4) TQ_LAUNCH(4);
-  else TQ_LAUNCH(8);
+  const int ring = fused_ring(dm, p);
+#define TQ_LAUNCH(RG, XB)                                                                                         \
+  hipLaunchKernelGGL((gemv_pq2_batch_kernel<RG, XB>), grid, block, (unsigned)stage, s, b, (int)dm.nsc, (int)dm.G8, \
+                     p.scw, p.spw, ws)
+  if (per_wave <= 2) { if (ring == 1) TQ_LAUNCH(1, 2); else TQ_LAUNCH(2, 2); }
+  else if (per_wave <= 4) { if (ring == 1) TQ_LAUNCH(1, 4); else TQ_LAUNCH(2, 4); }
+  else { if (ring == 1) TQ_LAUNCH(1, 8); else TQ_LAUNCH(2, 8); }
 #undef TQ_LAUNCH
   return hipGetLastError();
 }
