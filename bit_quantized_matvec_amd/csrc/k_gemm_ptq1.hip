@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
   uint32_t bs_in[4];
   float dx_in;
   auto load_side = [&](int sb) {
-    sc_in = scales[((size_t)tile * G8 + sb) * 64 + lane];
+    sc_in = scales[((size_t)tile * G8 + sb) * (kPtq1UnitBytes / 16) + lane];
     {
       const int n = (tid & 127) >> 3, g = min(sb * 8 + (tid & 7), G - 1);
       const size_t t = (size_t)min(tok0 + n, tokens - 1);
@@ -211,13 +211,13 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
   // uint4 D / 4 (the repacked [L][row] order); for pair p lane qd needs
   // X_a = D(12 p + qd), X_b = D(12 p + 6 + qd) and Y_a = D(12 p + 4 + qd),
   // Y_b = D(12 p + 10 + qd) (qd < 2) or the leftover D(48 + p) (qd >= 2).
-  const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) + ((size_t)tile * G8 * 13 * 64 + 16 * wave + r) * 16;
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) + (size_t)tile * G8 * kPtq1UnitBytes + (16 * wave + r) * 16;
   const int xa0 = 4 * qd, xb0 = (1 + (qd >> 1)) * 1024 + 4 * ((2 + qd) & 3);
   const int ya0 = qd < 2 ? 1024 + 4 * qd : 12 * 1024, yb0 = qd < 2 ? 2048 + 4 * (2 + qd) : 12 * 1024;
   const int ys = qd < 2 ? 3072 : 4;  // per pair
   uint32_t cdw[16], cdn[16];          // [pair][X_a, X_b, Y_a, Y_b]
   auto load_codes = [&](int sb) {
-    const uint8_t* b = cb + (size_t)sb * 13 * 1024;
+    const uint8_t* b = cb + (size_t)sb * kPtq1UnitBytes;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       cdn[4 * p] = *reinterpret_cast<const uint32_t*>(b + xa0 + 3072 * p);
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
 hipError_t launch_gemm_ptq1_mfma(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx,
                                  const int16_t* bsums, float* y, int32_t* idots, hipStream_t s) {
   const v4u* codes = reinterpret_cast<const v4u*>(w);
-  const v4u* scales = reinterpret_cast<const v4u*>(w + ptq1_code_bytes(dm));
+  const v4u* scales = reinterpret_cast<const v4u*>(w + kPtq1ScaleOffset);  // the first unit's scales
   // The token blocks go in grid.y, whose extent is kept below 2^16: longer
   // prompts are launched in chunks of 2^15 token blocks, each with its
   // tokens' activations and outputs.

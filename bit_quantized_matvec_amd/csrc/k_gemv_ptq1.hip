@@ -226,12 +226,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
     // is done: with every wave of the chip starting its superblock at once,
     // half the requests in flight stream faster than the whole superblock's
     // (measured on 32768 x 8192: 16.3 us -> 15.7-16.0 us).
-    const uint4* cp = codes + ((size_t)(tile * G8 + sb) * 13) * 64 + lane;
+    constexpr int kUnitU4 = (int)(kPtq1UnitBytes / 16);  // 13 code loads x 64 rows, then 64 scale rows
+    const uint4* cp = codes + (size_t)(tile * G8 + sb) * kUnitU4 + lane;
     uint4 cw[13];
 #pragma unroll
     for (int k = 0; k < 3; ++k) cw[k] = cp[k * 64];
     cw[12] = cp[12 * 64];
-    const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * 64 + lane];
+    const uint4 sc8 = scales[(size_t)(tile * G8 + sb) * kUnitU4 + lane];
 #pragma unroll
     for (int k = 3; k < 6; ++k) cw[k] = cp[k * 64];
     const uint4 left = cw[12];
@@ -462,7 +463,7 @@ hipError_t launch_gemv_ptq1_plan(const uint8_t* w, const Dims& dm, const int8_t*
                                  const int16_t* bsums, float* y, int32_t* idots, void* workspace, const GemvPlan& p,
                                  hipStream_t s) {
   const uint4* codes = reinterpret_cast<const uint4*>(w);
-  const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
+  const uint4* scales = reinterpret_cast<const uint4*>(w + kPtq1ScaleOffset);  // the first unit's scales
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const dim3 grid((unsigned)dm.ntiles, (unsigned)p.slices), block(64 * p.waves);
   launch_ptq1_nt<1>(idots != nullptr, grid, block, ptq1_lds_bytes(p.scw, 1), s, codes, scales, q, dx, bsums, y, idots,
@@ -497,7 +498,7 @@ hipError_t launch_gemm_ptq1(const uint8_t* w, const Dims& dm, int64_t tokens, co
   const GemvPlan p = plan_gemv_ptq1(dm, false);
   const int nt = ptq1_token_block(dm, tokens);
   const uint4* codes = reinterpret_cast<const uint4*>(w);
-  const uint4* scales = reinterpret_cast<const uint4*>(w + ptq1_code_bytes(dm));
+  const uint4* scales = reinterpret_cast<const uint4*>(w + kPtq1ScaleOffset);  // the first unit's scales
   const dim3 grid((unsigned)dm.ntiles, 1u, (unsigned)((tokens + nt - 1) / nt)), block(64 * p.waves);
   const size_t lds = ptq1_lds_bytes(p.scw, nt);
   const bool io = idots != nullptr;

@@ -122,7 +122,8 @@ __global__ void repack_pq2_scales(const uint8_t* __restrict__ src, uint32_t* __r
 }
 
 // ------------------------------------------------------------- ptq1_0 scales
-// fp16 scale of (row, group) into [tile][g8][row][8]; zero for padding.
+// fp16 scale of (row, group) into [row][8] of unit (tile, g8); zero for
+// padding.
 __global__ void repack_scales(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows, int64_t G,
                               int64_t G8, int block_bytes, int64_t n) {
   TQ_FOR_ITEMS(i, n) {
@@ -138,7 +139,7 @@ __global__ void repack_scales(const uint8_t* __restrict__ src, uint16_t* __restr
     const uint8_t* blk = src + (row * G + g) * block_bytes;
     h = (uint16_t)(blk[0] | (blk[1] << 8));
   }
-  dst[i] = h;
+  dst[rest * (kPtq1UnitBytes / 2) + kPtq1ScaleOffset / 2 + (i & 511)] = h;
   }
 }
 
@@ -176,12 +177,13 @@ __global__ void repack_ptq1_codes(const uint8_t* __restrict__ src, uint32_t* __r
       if (g < G) out |= (uint32_t)src[(row * G + g) * 28 + 2 + byte] << (8 * bi);
     }
   }
-  dst[i] = out;
+  // unit rest2 = tile * G8 + sb holds 13 * 256 code dwords, then its scales
+  dst[rest2 * (kPtq1UnitBytes / 4) + (i - rest2 * (kPtqLoads * 256))] = out;
   }
 }
 
-__global__ void unrepack_ptq1_codes(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                    uint8_t* __restrict__ dst, int64_t rows, int64_t G, int64_t G8) {
+__global__ void unrepack_ptq1_codes(const uint8_t* __restrict__ units, uint8_t* __restrict__ dst, int64_t rows, int64_t G,
+                                    int64_t G8) {
   TQ_FOR_ITEMS(b, rows * G) {
   const int64_t row = b / G, g = b % G;
   const int64_t tile = row / kRowTile;
@@ -189,10 +191,10 @@ __global__ void unrepack_ptq1_codes(const uint32_t* __restrict__ codes, const ui
   const int64_t sb = g / 8;
   const int gi = (int)(g % 8);
   uint8_t* out = dst + b * 28;
-  const uint16_t h = scales[((tile * G8 + sb) * 64 + r) * 8 + gi];
+  const uint8_t* base = units + (tile * G8 + sb) * kPtq1UnitBytes;
+  const uint16_t h = reinterpret_cast<const uint16_t*>(base + kPtq1ScaleOffset)[r * 8 + gi];
   out[0] = (uint8_t)(h & 0xff);
   out[1] = (uint8_t)(h >> 8);
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(codes);
   for (int byte = 0; byte < 26; ++byte) {
     int D, bi;
     if (byte < 24) {
@@ -203,7 +205,7 @@ __global__ void unrepack_ptq1_codes(const uint32_t* __restrict__ codes, const ui
       bi = 2 * (gi & 1) + (byte - 24);
     }
     const int L = D / 4, c = D % 4;
-    const int64_t dw = (((tile * G8 + sb) * kPtqLoads + L) * 64 + r) * 4 + c;
+    const int64_t dw = ((int64_t)L * 64 + r) * 4 + c;
     out[2 + byte] = base[dw * 4 + bi];
   }
   }
@@ -237,16 +239,14 @@ hipError_t launch_repack_ptq1(const uint8_t* src, uint8_t* dst, const Dims& dm, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ns = ptq1_scale_bytes(dm) / 2;
-  hipLaunchKernelGGL(repack_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src,
-                     reinterpret_cast<uint16_t*>(dst + ptq1_code_bytes(dm)), dm.rows, dm.G, dm.G8, 28, ns);
+  hipLaunchKernelGGL(repack_scales, dim3(grid_for(ns)), dim3(kThreads), 0, s, src, reinterpret_cast<uint16_t*>(dst),
+                     dm.rows, dm.G, dm.G8, 28, ns);
   return hipGetLastError();
 }
 
 hipError_t launch_unrepack_ptq1(const uint8_t* src, uint8_t* dst, const Dims& dm, hipStream_t s) {
   const int64_t nb = dm.rows * dm.G;
-  hipLaunchKernelGGL(unrepack_ptq1_codes, dim3(grid_for(nb)), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<const uint16_t*>(src + ptq1_code_bytes(dm)),
-                     dst, dm.rows, dm.G, dm.G8);
+  hipLaunchKernelGGL(unrepack_ptq1_codes, dim3(grid_for(nb)), dim3(kThreads), 0, s, src, dst, dm.rows, dm.G, dm.G8);
   return hipGetLastError();
 }
 

@@ -68,8 +68,14 @@ inline Dims dims(int64_t rows, int64_t cols) {
 constexpr int64_t kPq2UnitBytes = 4352;
 constexpr int64_t kPq2ScaleOffset = 4096;  // bytes from a unit's start to its scale pairs
 
-// Byte sizes of the repacked buffers (pq2_0: the code and scale shares of
-// its units).
+// ptq1_0 likewise: one unit per (row tile, 8-group superblock): its 13
+// code loads (uint4 [L][row], 13312 bytes), then its fp16 scales
+// ([row][8], 1024 bytes).
+constexpr int64_t kPtq1UnitBytes = 14336;
+constexpr int64_t kPtq1ScaleOffset = 13312;
+
+// Byte sizes of the repacked buffers (the code and scale shares of the
+// units).
 inline int64_t pq2_code_bytes(const Dims& d) { return d.ntiles * d.nsc * 4 * 64 * 16; }
 inline int64_t ptq1_code_bytes(const Dims& d) { return d.ntiles * d.G8 * kPtqLoads * 64 * 16; }
 inline int64_t pq2_scale_bytes(const Dims& d) { return d.ntiles * d.nsc * 64 * 4; }
