@@ -8,7 +8,9 @@
 // pq2_0 repacked
 //   Rows are grouped in tiles of 64 (padded with zero weights and zero
 //   scales).  Columns are grouped in superchunks of 256 (two 128-groups).
-//   codes: uint4 [tile][sc][qd 0..3][row 0..63]; within the 16 bytes, dword c
+//   One 4352-byte unit per (tile, sc), units tile-major: the codes (4096 B)
+//   then the scale pairs (256 B), so that a superchunk is one contiguous read.
+//   codes: uint4 [qd 0..3][row 0..63] of the unit; within the 16 bytes, dword c
 //     (0..3), byte j (0..3), 2-bit field s (bits 2s..2s+1) holds w, as a 2-bit
 //     two's-complement number (-1 -> 3, 0 -> 0, +1 -> 1), of column
 //         256*sc + 64*c + 16*qd + 4*s + j.
@@ -19,19 +21,22 @@
 //     activation dword.  For the MFMA path, lane (row, qd) holds dword c,
 //     whose four fields cover columns 64c + 16qd + [0, 16): a 16x16x64 MFMA
 //     takes chunk c of 16 rows and its B operand is 16 contiguous bytes of q.
-//   scales: uint32 [tile][sc][row 0..63]: the fp16 scales of groups 2 sc (low
+//   scales: uint32 [row 0..63] after the unit's codes: the fp16 scales of groups 2 sc (low
 //     half) and 2 sc + 1 (high half) of the row.  A wave with one row per lane
 //     reads a superchunk's scales as one 256-byte request; the MFMA path reads
 //     the pairs of four consecutive rows as one 16-byte load.
 //
 // ptq1_0 repacked (1.75 bits per weight kept, bytes only reordered)
-//   codes: uint4 [tile][sb][L 0..12][row 0..63], sb = superblock of 8 groups.
+//   One 14336-byte unit per (tile, sb), sb = superblock of 8 groups, units
+//   tile-major: the codes (13312 B) then the scales (1024 B).
+//   codes: uint4 [L 0..12][row 0..63] of the unit.
 //     The 52 dwords D = 4L + c of a row's superblock hold the 8 x 26 code
 //     bytes: D = 6*gi + m (gi < 8, m < 6) holds bytes 4m..4m+3 of group gi;
 //     D = 48 + p (p < 4) holds bytes 24, 25 of group 2p, then bytes 24, 25 of
 //     group 2p+1.  Bytes are copied unchanged (padding trits included).
-//   scales: fp16 [tile][sb][row 0..63][8]: the scale of group g of a row is
-//     entry g % 8 of slot g / 8 (groups padded to a multiple of 8 with 0).
+//   scales: fp16 [row 0..63][8] after the unit's codes: the scale of group g
+//     of a row is entry g % 8 of the unit of superblock g / 8 (groups padded
+//     to a multiple of 8 with 0).
 #pragma once
 #include <stdint.h>
 
