@@ -9,11 +9,14 @@
 //
 // How (gfx950):
 //   * v_mfma_i32_16x16x64_i8 on 16 tokens x 16 rows x 64 columns: lane
-//     (r, qd) = (lane % 16, lane / 16) supplies token r's and row r's
-//     columns 16 qd .. 16 qd + 15 of each 64-column step.  The row side comes
-//     from one 16-byte code load per row block and superchunk (dword c = step
-//     c, one shift and one mask per 2-bit field); the token side is 16 bytes
-//     of q per token.
+//     (r, qd) = (lane % 16, lane / 16) supplies the columns 16 qd .. 16 qd + 15
+//     of each 64-column step for row r and for the token in MFMA row r.  The
+//     row side comes from one 16-byte code load per row block and superchunk
+//     (dword c = step c, one shift and one mask per 2-bit field); the token
+//     side is 16 bytes of q per token.  Token t of a block of 16 sits in MFMA
+//     row 4 (t % 4) + t / 4, so result slot v of lane (r, qd) holds token
+//     4 v + qd: with at most 4 (8) tokens only slot 0 (slots 0 and 1) hold
+//     real tokens, and the epilogue and the final run sums skip the others.
 //   * Work split.  The matrix-vector product sums each row's superchunks in
 //     runs (one run per wave of its plan without a workspace) and adds the
 //     runs in order.  Here each wave owns one run, for all the row blocks
@@ -110,15 +113,17 @@ struct GemmShape {
 // Block = nruns waves; wave w sums superchunks [w spw, min(nsc, (w + 1) spw)).
 // The MFMA's first operand is the activations (16 tokens x 64 columns), the
 // second the expanded codes (64 columns x 16 rows): lane (l16, qd) of the
-// result holds tokens 4 qd .. 4 qd + 3 of row l16, so a lane needs one scale
-// pair per row block, and 16 consecutive rows of a token are stored together.
+// result holds tokens qd, 4 + qd, 8 + qd, 12 + qd of row l16 (slots 0..VT-1
+// of them are used), so a lane needs one scale pair per row block, and 16
+// consecutive rows of a token are stored together.
 // Every operand streams through a ring of RD superchunks in registers.
-template <int NT, int RD, int MRB, bool IDOTS>
+template <int NT, int RD, int MRB, int VT, bool IDOTS>
 __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
     const v4u* __restrict__ codes, const int8_t* __restrict__ q,
     const float* __restrict__ dx, float* __restrict__ y, int32_t* __restrict__ idots, int rows, int nsc, int tokens,
     int spw, GemmShape gs) {
-  constexpr int kAcc = MRB * NT * 4;  // fp64 sums per lane
+  static_assert(VT == 1 || VT == 2 || VT == 4, "result slots per lane");
+  constexpr int kAcc = MRB * NT * VT;  // fp64 sums per lane
   extern __shared__ double sums[];       // run sums of one phase [wave][kPer][lane]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,8 +161,8 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
   // byte offsets: codes of row block i at superchunk sc are at a_off[i] +
   // kUnit sc, lane (l16, qd) reading 16 bytes at (64 qd + l16) * 16; its
   // scale pair at s_off[i] + kUnit sc + 4 l16; token block nb's activations at
-  // (16 nb + l16) K + 16 qd + 256 sc + 64 c; d_x of token `lane` at 4 (lane
-  // nsc + sc), lanes past 16 NT out of range
+  // (16 nb + trow) K + 16 qd + 256 sc + 64 c, trow the token in MFMA row l16;
+  // d_x of token `lane` at 4 (lane nsc + sc), lanes past 16 NT out of range
   int a_off[MRB], s_off[MRB];
 #pragma unroll
   for (int i = 0; i < MRB; ++i) {
@@ -166,6 +171,7 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
     s_off[i] = tl * nsc * kUnit + 16 * rbi * 4;
   }
   const int a_lane = (64 * qd + l16) * 16, s_lane = 4 * l16;
+  const int trow = 4 * (l16 & 3) + (l16 >> 2);
   const int x_lane = lane < 16 * NT ? 4 * lane * nsc : 0x7fffff00;
 
   v4u ra[RD][MRB];
@@ -183,31 +189,31 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
     }
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb) {
-      const int vo = (16 * nb + l16) * K + 16 * qd;
+      const int vo = (16 * nb + trow) * K + 16 * qd;
 #pragma unroll
       for (int c = 0; c < 4; ++c) rb[J][nb][c] = load16(real ? b_buf : none, vo + 64 * c, 256 * sc);
     }
     if (!IDOTS) rx[J] = __builtin_bit_cast(float, load4(real ? x_buf : none, x_lane, 4 * sc));
   };
 
-  double yacc[MRB][NT][4];
+  double yacc[MRB][NT][VT];
 #pragma unroll
   for (int i = 0; i < MRB; ++i)
 #pragma unroll
     for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) yacc[i][nb][v] = 0.0;
+      for (int v = 0; v < VT; ++v) yacc[i][nb][v] = 0.0;
 
   auto step = [&](int J, int j) __attribute__((always_inline)) {
-    double xd[NT][4];
+    double xd[NT][VT];
     if (!IDOTS) {
-      // d_x of token 16 nb + 4 qd + v, from the lane that loaded it
+      // d_x of token 16 nb + 4 v + qd, from the lane that loaded it
       const int xi = __builtin_bit_cast(int, rx[J]);
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          xd[nb][v] = (double)__builtin_bit_cast(float, __shfl(xi, 16 * nb + 4 * qd + v, 64)) * 0.015625;
+        for (int v = 0; v < VT; ++v)
+          xd[nb][v] = (double)__builtin_bit_cast(float, __shfl(xi, 16 * nb + 4 * v + qd, 64)) * 0.015625;
     }
     const int sc = sc0 + j;
 #pragma unroll
@@ -229,8 +235,8 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
         for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int t = tok0 + 16 * nb + 4 * qd + v;
+          for (int v = 0; v < VT; ++v) {
+            const int t = tok0 + 16 * nb + 4 * v + qd;
             if (t < tokens && row < rows) {
               int32_t* o = idots + ((size_t)t * rows + row) * G + 2 * sc;
               o[0] = acc[nb][0][v] >> 6;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
         for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+          for (int v = 0; v < VT; ++v) {
             const double inner = __builtin_fma(d1, (double)acc[nb][1][v], d0 * (double)acc[nb][0][v]);
             yacc[i][nb][v] = __builtin_fma(xd[nb][v], inner, yacc[i][nb][v]);
           }
@@ -286,25 +292,25 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int sl = (i * NT + nb) * 4 + v;
+        for (int v = 0; v < VT; ++v) {
+          const int sl = (i * NT + nb) * VT + v;
           if (sl / kPer == p) sums[((size_t)wave * kPer + sl % kPer) * 64 + lane] = yacc[i][nb][v];
         }
     __syncthreads();
     for (int sl = p * kPer + wave; sl < (p + 1) * kPer; sl += nruns) {
-      const int i = sl / (NT * 4), nb = (sl / 4) % NT, v = sl % 4;
+      const int i = sl / (NT * VT), nb = (sl / VT) % NT, v = sl % VT;
       if (i >= nrb) continue;
       double t = sums[(size_t)(sl % kPer) * 64 + lane];
       for (int w = 1; w < nruns; ++w) t += sums[((size_t)w * kPer + sl % kPer) * 64 + lane];
-      const int row = (b0 + i) * 16 + l16, tk = tok0 + 16 * nb + 4 * qd + v;
+      const int row = (b0 + i) * 16 + l16, tk = tok0 + 16 * nb + 4 * v + qd;
       if (row < rows && tk < tokens) y[(size_t)tk * rows + row] = (float)t;
     }
   }
 }
 
-template <int NT, int MRB>
+template <int NT, int MRB, int VT>
 size_t gemm_lds_bytes(int nruns) {
-  constexpr int acc = MRB * NT * 4;
+  constexpr int acc = MRB * NT * VT;
   return (size_t)nruns * (acc > 20 ? acc / 2 : acc) * 64 * 8;
 }
 
@@ -322,20 +328,20 @@ GemmShape gemm_shape(const Dims& dm, int64_t tokens, int nt, int mrb, int min_gr
   return gs;
 }
 
-template <int NT, int RD, int MRB>
+template <int NT, int RD, int MRB, int VT>
 hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
                          int32_t* idots, int min_groups, hipStream_t s) {
   const GemmShape gs = gemm_shape(dm, tokens, NT, MRB, min_groups);
   const GemvPlan p = plan_gemv_pq2(dm, false);  // the runs of the matrix-vector product
   const int nruns = (int)((dm.nsc + p.spw - 1) / p.spw);
   const dim3 grid((unsigned)((int64_t)gs.nrg * gs.ntg)), block(64 * nruns);
-  const size_t lds = gemm_lds_bytes<NT, MRB>(nruns);
+  const size_t lds = gemm_lds_bytes<NT, MRB, VT>(nruns);
   const v4u* codes = reinterpret_cast<const v4u*>(w);
   if (idots)
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, true>), grid, block, lds, s, codes, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, VT, true>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   else
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, false>), grid, block, lds, s, codes, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, VT, false>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   return hipGetLastError();
 }
@@ -346,7 +352,8 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
                            int32_t* idots, hipStream_t s) {
   static_assert(kMaxRuns == 4, "the matrix-vector plan uses at most 4 waves per row tile");
   // Up to 16 tokens: one MFMA token block per workgroup, a ring two
-  // superchunks deep; more: token groups of 32 (two blocks), one superchunk
+  // superchunks deep, and up to 4 (8) tokens only the result slots that hold
+  // real tokens are finished; more: token groups of 32 (two blocks), one superchunk
   // in flight per wave (the other wave on the SIMD covers its latency).  One
   // launch covers at most 2^22 workgroups (far below 2^32 work-items);
   // longer prompts go in chunks of whole token groups, each with its tokens'
@@ -365,8 +372,11 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
     const float* dxc = dx ? dx + t0 * dm.nsc : nullptr;
     float* yc = y ? y + t0 * dm.rows : nullptr;
     int32_t* ic = idots ? idots + t0 * dm.rows * 2 * dm.nsc : nullptr;
-    const hipError_t e = nt == 1 ? launch_gemm_t<1, 2, kRbSmall>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
-                                 : launch_gemm_t<2, 1, kMaxRb>(w, dm, tc, qc, dxc, yc, ic, kMinRowGroups, s);
+    const hipError_t e =
+        nt == 2    ? launch_gemm_t<2, 1, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, kMinRowGroups, s)
+        : tc <= 4  ? launch_gemm_t<1, 2, kRbSmall, 1>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
+        : tc <= 8  ? launch_gemm_t<1, 2, kRbSmall, 2>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
+                   : launch_gemm_t<1, 2, kRbSmall, 4>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
