@@ -38,7 +38,8 @@
 //     run, a row block past the range, a token past the end) reads an empty
 //     or short resource and returns zeros without touching memory.  All
 //     loads are unconditional, so the compiler's wait counts follow the ring
-//     slot by slot.
+//     slot by slot.  Up to 16 tokens the activations (cache hits) have a
+//     ring of their own, one slot deep and issued ahead of the codes.
 //   * Epilogue per superchunk, in fp64 (every product exact, sums rounded
 //     once per operation): inner = d_w(2sc+1) * I1 + d_w(2sc) * I0, then
 //     y += (d_x / 64) * inner; the MFMA sums are 64 I (two's-complement codes
@@ -117,7 +118,7 @@ struct GemmShape {
 // of them are used), so a lane needs one scale pair per row block, and 16
 // consecutive rows of a token are stored together.
 // Every operand streams through a ring of RD superchunks in registers.
-template <int NT, int RD, int MRB, int VT, bool IDOTS>
+template <int NT, int RD, bool SPLIT, int MRB, int VT, bool IDOTS>
 __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
     const v4u* __restrict__ codes, const int8_t* __restrict__ q,
     const float* __restrict__ dx, float* __restrict__ y, int32_t* __restrict__ idots, int rows, int nsc, int tokens,
@@ -174,26 +175,36 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
   const int trow = 4 * (l16 & 3) + (l16 >> 2);
   const int x_lane = lane < 16 * NT ? 4 * lane * nsc : 0x7fffff00;
 
+  // Ring slots: RD for the codes and scales; RD for the activations and d_x,
+  // or one with SPLIT (see the loop below).
+  constexpr int RA = SPLIT ? 1 : RD;
   v4u ra[RD][MRB];
   uint32_t rs[RD][MRB];
-  v4u rb[RD][NT][4];
-  float rx[RD];
-  auto fetch = [&](int J, int k) __attribute__((always_inline)) {
+  v4u rb[RA][NT][4];
+  float rx[RA];
+  // Loads of superchunk k: its codes and scale pairs into code slot J and/or
+  // its activations and d_x into activation slot JA (one lambda: two nested
+  // ones made the compiler keep 58 more VGPRs live).
+  auto fetch = [&](int J, int JA, int k, bool codes, bool acts) __attribute__((always_inline)) {
     const bool real = k < n;  // uniform
     const int sc = sc0 + k;
+    if (codes) {
 #pragma unroll
-    for (int i = 0; i < MRB; ++i) {
-      const bool use = real && i < nrb;
-      ra[J][i] = load16_nt(use ? a_buf : none, a_lane, a_off[i] + kUnit * sc);
-      if (!IDOTS) rs[J][i] = load4(use ? s_buf : none, s_lane, s_off[i] + kUnit * sc);
+      for (int i = 0; i < MRB; ++i) {
+        const bool use = real && i < nrb;
+        ra[J][i] = load16_nt(use ? a_buf : none, a_lane, a_off[i] + kUnit * sc);
+        if (!IDOTS) rs[J][i] = load4(use ? s_buf : none, s_lane, s_off[i] + kUnit * sc);
+      }
     }
+    if (acts) {
 #pragma unroll
-    for (int nb = 0; nb < NT; ++nb) {
-      const int vo = (16 * nb + trow) * K + 16 * qd;
+      for (int nb = 0; nb < NT; ++nb) {
+        const int vo = (16 * nb + trow) * K + 16 * qd;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rb[J][nb][c] = load16(real ? b_buf : none, vo + 64 * c, 256 * sc);
+        for (int c = 0; c < 4; ++c) rb[JA][nb][c] = load16(real ? b_buf : none, vo + 64 * c, 256 * sc);
+      }
+      if (!IDOTS) rx[JA] = __builtin_bit_cast(float, load4(real ? x_buf : none, x_lane, 4 * sc));
     }
-    if (!IDOTS) rx[J] = __builtin_bit_cast(float, load4(real ? x_buf : none, x_lane, 4 * sc));
   };
 
   double yacc[MRB][NT][VT];
@@ -204,11 +215,12 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
       for (int v = 0; v < VT; ++v) yacc[i][nb][v] = 0.0;
 
-  auto step = [&](int J, int j) __attribute__((always_inline)) {
+  // superchunk j from code slot J and activation slot JA
+  auto step = [&](int J, int JA, int j) __attribute__((always_inline)) {
     double xd[NT][VT];
     if (!IDOTS) {
       // d_x of token 16 nb + 4 v + qd, from the lane that loaded it
-      const int xi = __builtin_bit_cast(int, rx[J]);
+      const int xi = __builtin_bit_cast(int, rx[JA]);
 #pragma unroll
       for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
 #pragma unroll
         for (int nb = 0; nb < NT; ++nb)
           acc[nb][c >> 1] =
-              __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, rb[J][nb][c]), a, acc[nb][c >> 1], 0, 0, 0);
+              __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, rb[JA][nb][c]), a, acc[nb][c >> 1], 0, 0, 0);
       }
       const int row = (b0 + i) * 16 + l16;
       if (IDOTS) {
@@ -260,21 +272,46 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
   // the loop consumes slots 0 .. RD-1 and refills each RD superchunks ahead,
   // and the last n mod RD superchunks sit in slots 0, 1, ... after it.  No
   // step inside the loop is conditional, so the compiler's wait counts stay
-  // per slot instead of draining the ring at a join.
-#pragma unroll
-  for (int J = 0; J < RD; ++J) fetch(J, J);
+  // per slot instead of draining the ring at a join.  Vector loads complete
+  // in issue order, so a wait for one load is a wait for every earlier one.
+  //   * Plain: superchunk k's codes then its activations, RD ahead.
+  //   * SPLIT: the codes RD ahead, the activations (cache hits, one slot) one
+  //     ahead and issued before the codes of the same pass, so that waiting
+  //     for them never waits for the codes' HBM round trip.
   const int full = n / RD;
-  for (int c = 0; c < full; ++c) {
-#pragma unroll
-    for (int J = 0; J < RD; ++J) {
-      step(J, c * RD + J);
-      fetch(J, c * RD + J + RD);
-    }
-  }
   const int left = n - full * RD;
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int J = 0; J + 1 < RD; ++J)
-    if (J < left) step(J, full * RD + J);  // uniform
+    for (int J = 0; J < RD; ++J) fetch(J, J, J, true, true);
+    for (int c = 0; c < full; ++c) {
+#pragma unroll
+      for (int J = 0; J < RD; ++J) {
+        step(J, J, c * RD + J);
+        fetch(J, J, c * RD + J + RD, true, true);
+      }
+    }
+#pragma unroll
+    for (int J = 0; J + 1 < RD; ++J)
+      if (J < left) step(J, J, full * RD + J);  // uniform
+  } else {
+    fetch(0, 0, 0, true, true);
+#pragma unroll
+    for (int J = 1; J < RD; ++J) fetch(J, 0, J, true, false);
+    for (int c = 0; c < full; ++c) {
+#pragma unroll
+      for (int J = 0; J < RD; ++J) {
+        step(J, 0, c * RD + J);
+        fetch(J, 0, c * RD + J + 1, false, true);
+        fetch(J, 0, c * RD + J + RD, true, false);
+      }
+    }
+#pragma unroll
+    for (int J = 0; J + 1 < RD; ++J)
+      if (J < left) {  // uniform
+        step(J, 0, full * RD + J);
+        fetch(J, 0, full * RD + J + 1, false, true);
+      }
+  }
   if (IDOTS) return;
 
   // Runs added in run order: y = ((s0 + s1) + s2) + s3, each token's order in
@@ -328,7 +365,7 @@ GemmShape gemm_shape(const Dims& dm, int64_t tokens, int nt, int mrb, int min_gr
   return gs;
 }
 
-template <int NT, int RD, int MRB, int VT>
+template <int NT, int RD, bool SPLIT, int MRB, int VT>
 hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
                          int32_t* idots, int min_groups, hipStream_t s) {
   const GemmShape gs = gemm_shape(dm, tokens, NT, MRB, min_groups);
@@ -338,10 +375,10 @@ hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const
   const size_t lds = gemm_lds_bytes<NT, MRB, VT>(nruns);
   const v4u* codes = reinterpret_cast<const v4u*>(w);
   if (idots)
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, VT, true>), grid, block, lds, s, codes, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, SPLIT, MRB, VT, true>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   else
-    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, MRB, VT, false>), grid, block, lds, s, codes, q, dx, y, idots,
+    hipLaunchKernelGGL((gemm_pq2_kernel<NT, RD, SPLIT, MRB, VT, false>), grid, block, lds, s, codes, q, dx, y, idots,
                        (int)dm.rows, (int)dm.nsc, (int)tokens, p.spw, gs);
   return hipGetLastError();
 }
@@ -351,10 +388,12 @@ hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const
 hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
                            int32_t* idots, hipStream_t s) {
   static_assert(kMaxRuns == 4, "the matrix-vector plan uses at most 4 waves per row tile");
-  // Up to 16 tokens: one MFMA token block per workgroup, a ring two
-  // superchunks deep, and up to 4 (8) tokens only the result slots that hold
-  // real tokens are finished; more: token groups of 32 (two blocks), one superchunk
-  // in flight per wave (the other wave on the SIMD covers its latency).  One
+  // Up to 16 tokens: one MFMA token block per workgroup, codes two
+  // superchunks ahead and activations one (17408 x 5120 at 4 tokens: 7.8 us
+  // with both two ahead, 7.5 split), and up to 4 (8) tokens only the result
+  // slots that hold real tokens are finished; more: token groups of 32 (two
+  // blocks), one superchunk in flight per wave (the other wave on the SIMD
+  // covers its latency).  One
   // launch covers at most 2^22 workgroups (far below 2^32 work-items);
   // longer prompts go in chunks of whole token groups, each with its tokens'
   // activations and outputs.  The token grouping does not change the
@@ -373,10 +412,10 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
     float* yc = y ? y + t0 * dm.rows : nullptr;
     int32_t* ic = idots ? idots + t0 * dm.rows * 2 * dm.nsc : nullptr;
     const hipError_t e =
-        nt == 2    ? launch_gemm_t<2, 1, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, kMinRowGroups, s)
-        : tc <= 4  ? launch_gemm_t<1, 2, kRbSmall, 1>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
-        : tc <= 8  ? launch_gemm_t<1, 2, kRbSmall, 2>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
-                   : launch_gemm_t<1, 2, kRbSmall, 4>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s);
+        nt == 2    ? launch_gemm_t<2, 1, false, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, kMinRowGroups, s)
+        : tc <= 4  ? launch_gemm_t<1, 2, true, kRbSmall, 1>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
+        : tc <= 8  ? launch_gemm_t<1, 2, true, kRbSmall, 2>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
+                   : launch_gemm_t<1, 2, true, kRbSmall, 4>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
