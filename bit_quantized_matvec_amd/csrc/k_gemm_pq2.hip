@@ -26,10 +26,11 @@
 //     bit for bit.
 //   * Rows: the 16-row blocks of the matrix are split into contiguous,
 //     nearly equal ranges.  Up to 16 tokens: ranges of at most 3 blocks, at
-//     least 512 of them, two workgroups per compute unit.  More tokens:
+//     least 512 of them, two workgroups per compute unit.  17 to 48 tokens:
 //     ranges of at most 5 blocks, at least 256, each range once per group of
-//     32 tokens, again two workgroups per compute unit.  A wave's fp64 sums
-//     (5 row blocks x 32 tokens) fill a third of its registers.
+//     16 tokens.  More: the same ranges once per group of 32 tokens, again
+//     two workgroups per compute unit.  A wave's fp64 sums (5 row blocks x
+//     32 tokens) fill a third of its registers.
 //   * Data flow per wave: every operand (codes, scale pairs, activations,
 //     d_x) streams through a ring of RD superchunks in registers by raw
 //     buffer loads: a per-lane offset, a uniform offset and a resource over
@@ -388,22 +389,29 @@ hipError_t launch_gemm_t(const uint8_t* w, const Dims& dm, int64_t tokens, const
 hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, const int8_t* q, const float* dx, float* y,
                            int32_t* idots, hipStream_t s) {
   static_assert(kMaxRuns == 4, "the matrix-vector plan uses at most 4 waves per row tile");
-  // Up to 16 tokens: one MFMA token block per workgroup, codes two
-  // superchunks ahead and activations one (17408 x 5120 at 4 tokens: 7.8 us
-  // with both two ahead, 7.5 split), and up to 4 (8) tokens only the result
-  // slots that hold real tokens are finished; more: token groups of 32 (two
-  // blocks), one superchunk in flight per wave (the other wave on the SIMD
-  // covers its latency).  One
-  // launch covers at most 2^22 workgroups (far below 2^32 work-items);
+  // Token groups and row ranges, measured on 17408 x 5120 (2 tokens per
+  // point, us): up to 16 tokens one group of 16 over ranges of at most 3
+  // blocks (at least 512 ranges), codes two superchunks ahead and
+  // activations one (at 4 tokens 7.8 with both two ahead, 7.5 split), and up
+  // to 4 (8) tokens only the result slots that hold real tokens are
+  // finished; 17 to 48 tokens groups of 16 over ranges of at most 5 blocks
+  // (at least 256), two or three groups keeping two workgroups per compute
+  // unit (17 / 32 / 48 tokens: 13.5 / 13.7 / 17.9, one or two groups of 32:
+  // 14.7 / 15.5 / 19.2); more, groups of 32 (two MFMA blocks) over ranges of
+  // at most 5 blocks, one superchunk in flight per wave, the other wave on
+  // the SIMD covering its latency (64 tokens: 19.3, groups of 16: 22.4).
+  // One launch covers at most 2^22 workgroups (far below 2^32 work-items);
   // longer prompts go in chunks of whole token groups, each with its tokens'
   // activations and outputs.  The token grouping does not change the
   // summation order.  Buffer offsets are 32-bit: the largest, 32 tokens of
   // activations, is 32 cols bytes.
   if (dm.cols > (int64_t(1) << 25)) return hipErrorInvalidValue;
-  const int nt = tokens <= 16 ? 1 : 2;
-  const int mrb = nt == 1 ? kRbSmall : kMaxRb;
+  const int mode = tokens <= 16 ? 0 : tokens <= 48 ? 1 : 2;  // fixed for every chunk
+  const int nt = mode == 2 ? 2 : 1;
+  const int mrb = mode == 0 ? kRbSmall : kMaxRb;
+  const int ranges = mode == 0 ? 2 * kMinRowGroups : kMinRowGroups;
   const int64_t group = 16 * nt;
-  const int64_t rgs = gemm_shape(dm, 1, nt, mrb, nt == 1 ? 2 * kMinRowGroups : kMinRowGroups).nrg;
+  const int64_t rgs = gemm_shape(dm, 1, nt, mrb, ranges).nrg;
   const int64_t chunk = std::max<int64_t>(1, (int64_t(1) << 22) / rgs) * group;
   for (int64_t t0 = 0; t0 < tokens; t0 += chunk) {
     const int64_t tc = std::min(chunk, tokens - t0);
@@ -412,10 +420,11 @@ hipError_t launch_gemm_pq2(const uint8_t* w, const Dims& dm, int64_t tokens, con
     float* yc = y ? y + t0 * dm.rows : nullptr;
     int32_t* ic = idots ? idots + t0 * dm.rows * 2 * dm.nsc : nullptr;
     const hipError_t e =
-        nt == 2    ? launch_gemm_t<2, 1, false, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, kMinRowGroups, s)
-        : tc <= 4  ? launch_gemm_t<1, 2, true, kRbSmall, 1>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
-        : tc <= 8  ? launch_gemm_t<1, 2, true, kRbSmall, 2>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s)
-                   : launch_gemm_t<1, 2, true, kRbSmall, 4>(w, dm, tc, qc, dxc, yc, ic, 2 * kMinRowGroups, s);
+        mode == 2  ? launch_gemm_t<2, 1, false, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, ranges, s)
+        : mode == 1 ? launch_gemm_t<1, 2, true, kMaxRb, 4>(w, dm, tc, qc, dxc, yc, ic, ranges, s)
+        : tc <= 4  ? launch_gemm_t<1, 2, true, kRbSmall, 1>(w, dm, tc, qc, dxc, yc, ic, ranges, s)
+        : tc <= 8  ? launch_gemm_t<1, 2, true, kRbSmall, 2>(w, dm, tc, qc, dxc, yc, ic, ranges, s)
+                   : launch_gemm_t<1, 2, true, kRbSmall, 4>(w, dm, tc, qc, dxc, yc, ic, ranges, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
