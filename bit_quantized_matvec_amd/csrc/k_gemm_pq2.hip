@@ -338,8 +338,15 @@ __global__ __launch_bounds__(64 * kMaxRuns, IDOTS ? 1 : 2) void gemm_pq2_kernel(
     for (int sl = p * kPer + wave; sl < (p + 1) * kPer; sl += nruns) {
       const int i = sl / (NT * VT), nb = (sl / VT) % NT, v = sl % VT;
       if (i >= nrb) continue;
-      double t = sums[(size_t)(sl % kPer) * 64 + lane];
-      for (int w = 1; w < nruns; ++w) t += sums[((size_t)w * kPer + sl % kPer) * 64 + lane];
+      // every run's sum read before the first add (a read and an add per run
+      // waited an LDS round trip each); runs past the last repeat it unused
+      double rv[kMaxRuns];
+#pragma unroll
+      for (int w = 0; w < kMaxRuns; ++w) rv[w] = sums[((size_t)min(w, nruns - 1) * kPer + sl % kPer) * 64 + lane];
+      double t = rv[0];
+#pragma unroll
+      for (int w = 1; w < kMaxRuns; ++w)
+        if (w < nruns) t += rv[w];
       const int row = (b0 + i) * 16 + l16, tk = tok0 + 16 * nb + 4 * v + qd;
       if (row < rows && tk < tokens) y[(size_t)tk * rows + row] = (float)t;
     }

@@ -283,9 +283,17 @@ __device__ __forceinline__ void gemv_pq2_body(const uint4* __restrict__ codes, c
   prev = __shfl(prev, 0, 64);
   if (prev != (unsigned)(nslices - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // every slice's partial is requested before the first add (one loop with
+  // a load and an add per slice waited a full round trip per slice); the
+  // indices past the last slice repeat it and are not added
+  double pv[kMaxSlices];
+#pragma unroll
+  for (int k = 0; k < kMaxSlices; ++k)
+    pv[k] = __hip_atomic_load(&partials[min(k, nslices - 1) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   double t = 0.0;
-  for (int k = 0; k < nslices; ++k)
-    t += __hip_atomic_load(&partials[k * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int k = 0; k < kMaxSlices; ++k)
+    if (k < nslices) t += pv[k];
   if (row < rows) y[row] = (float)t;
   if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

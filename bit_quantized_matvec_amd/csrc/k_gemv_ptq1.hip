@@ -409,9 +409,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_ptq1_kernel(const uint4* 
   prev = __shfl(prev, 0, 64);
   if (prev != (unsigned)(nslices - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  double t = __hip_atomic_load(&partials[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int sb = 1; sb < G8; ++sb)
-    t += __hip_atomic_load(&partials[sb * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // eight superblock sums requested at a time before they are added (one
+  // load and one add per superblock waited a full round trip each); indices
+  // past the last superblock repeat it and are not added
+  double t = 0.0;
+  for (int sb0 = 0; sb0 < G8; sb0 += 8) {
+    double pv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      pv[k] = __hip_atomic_load(&partials[min(sb0 + k, G8 - 1) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (sb0 + k < G8) t = sb0 + k == 0 ? pv[0] : t + pv[k];
+  }
   if (row < rows) y[row] = (float)t;
   if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
