@@ -39,8 +39,9 @@
 //     run, a row block past the range, a token past the end) reads an empty
 //     or short resource and returns zeros without touching memory.  All
 //     loads are unconditional, so the compiler's wait counts follow the ring
-//     slot by slot.  Up to 16 tokens the activations (cache hits) have a
-//     ring of their own, one slot deep and issued ahead of the codes.
+//     slot by slot.  With 16-token groups (up to 48 tokens) the activations
+//     (cache hits) have a ring of their own, one slot deep and issued ahead
+//     of the codes.
 //   * Epilogue per superchunk, in fp64 (every product exact, sums rounded
 //     once per operation): inner = d_w(2sc+1) * I1 + d_w(2sc) * I0, then
 //     y += (d_x / 64) * inner; the MFMA sums are 64 I (two's-complement codes
