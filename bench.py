@@ -441,13 +441,14 @@ def source_sha256(files) -> str:
 
 # the sources each benchmarked kernel is compiled from: a recorded counter
 # figure is reported only while their hash matches
+# (with the build script, which holds the compiler flags)
 KERNEL_SOURCES = {
-    "gemv_pq2_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h"],
-    "gemv_pq2_batch_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h"],
-    "gemm_pq2_kernel": ["k_gemm_pq2.hip", "kernels.h", "layout.h"],
-    "gemv_ptq1_kernel": ["k_gemv_ptq1.hip", "kernels.h", "layout.h"],
-    "gemm_ptq1_kernel": ["k_gemm_ptq1.hip", "kernels.h", "layout.h"],
-    "quantize_q8k_kernel": ["k_quant.hip", "q8k_block.h", "kernels.h"],
+    "gemv_pq2_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h", "../build.py"],
+    "gemv_pq2_batch_kernel": ["k_gemv_pq2.hip", "q8k_block.h", "kernels.h", "layout.h", "../build.py"],
+    "gemm_pq2_kernel": ["k_gemm_pq2.hip", "kernels.h", "layout.h", "../build.py"],
+    "gemv_ptq1_kernel": ["k_gemv_ptq1.hip", "kernels.h", "layout.h", "../build.py"],
+    "gemm_ptq1_kernel": ["k_gemm_ptq1.hip", "kernels.h", "layout.h", "../build.py"],
+    "quantize_q8k_kernel": ["k_quant.hip", "q8k_block.h", "kernels.h", "../build.py"],
 }
 
 

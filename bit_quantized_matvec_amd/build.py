@@ -29,9 +29,10 @@ FLAGS = [
     "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source extras: the MFMA kernel keeps its accumulators in ordinary VGPRs,
-# so the epilogue reads them without v_accvgpr_read copies.
-EXTRA = {"k_gemm_pq2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras: the MFMA kernels keep their accumulators in ordinary
+# VGPRs, so the epilogues read them without v_accvgpr_read copies.
+EXTRA = {"k_gemm_pq2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_gemm_ptq1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, out: str, extra=()) -> None:
