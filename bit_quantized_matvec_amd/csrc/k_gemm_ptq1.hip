@@ -21,21 +21,21 @@
 //     trits of byte 25), so C = the group's sum of trit x q and the integer
 //     dot is C minus the group's sum of q (trit = w + 1).
 //   * B is the matching permutation of q: for trit dword (c, j) the four
-//     activations 5 apart, q[20 c + j + 5 i], i = 0..3.  Per superblock the
-//     workgroup copies its tokens' q into LDS (direct global-to-LDS loads,
-//     issued a superblock ahead), then its threads build the B pieces (a
-//     4 x 5 byte transpose per code dword) in [group][step][token][qd]
-//     order, so that one MFMA's B is one 16-byte read per lane.
+//     activations 5 apart, q[20 c + j + 5 i], i = 0..3.  Per superblock each
+//     lane builds the three B pieces of one (token, slot) for two groups from
+//     40 bytes of q held in registers (loaded a superblock ahead, two byte
+//     permutes per entry) and stores them in [group][step][token][qd] order,
+//     so that one MFMA's B is one 16-byte read per lane.
 //   * The fp64 epilogue per group pair (groups 2p, 2p + 1 share d_x):
 //     inner = d_w(2p+1) I1 + d_w(2p) I0 (one rounding), acc = d_x inner + acc
 //     (one rounding), acc from zero per superblock, superblock sums added in
 //     order.  The matrix-vector product uses the same sequence, so every
 //     token's output is bit-identical to it.
-//   * Workgroup = 4 waves = one 64-row tile and 16 tokens (45 KiB of LDS:
-//     three workgroups per compute unit); each lane loads exactly the code
-//     dwords it decodes (16 per superblock), and those and the staging
-//     inputs of the next superblock are loaded while the current ones are
-//     used.
+//   * Workgroup = 4 waves = one 64-row tile and 16 tokens (29 KiB of LDS,
+//     142 VGPRs: three workgroups per compute unit); each lane loads exactly
+//     the code dwords it decodes (16 per superblock), and those and the q
+//     bytes and scales of the next superblock are loaded while the current
+//     ones are used.
 //   * Tokens past the end read a valid token (the last) and rows past the
 //     end have zero codes and scales; neither is stored.
 #include <algorithm>
@@ -52,7 +52,6 @@ constexpr int kTok = 16;  // tokens per workgroup (MFMA columns)
 
 struct Stage {
   v4u bimg[8][3][kTok][4];  // B pieces [group][step][token][qd], 24 KiB
-  v4u raw[kTok][64];        // the superblock's q of each token, 16 KiB
   double dw[8][64];         // d_w [group][row of the tile], 4 KiB
   int qs[8][kTok];          // sum of q per group
   double dxs[4][kTok];      // d_x per q8_K block of the superblock
@@ -101,24 +100,28 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
   const int tok0 = blockIdx.y * kTok;
   const size_t K = (size_t)G * 128;
 
-  // B pieces that no task writes stay zero: qd = 3's Y slots and the last
-  // two slots of step 2
-  {
-    v4u* b = &st.bimg[0][0][0][0];
-    for (int i = tid; i < 8 * 3 * kTok * 4; i += 256) b[i] = v4u{0u, 0u, 0u, 0u};
-  }
-
   // ---- staging inputs of a superblock, loaded a superblock ahead
-  // q: 16 tokens x 1 KiB by direct global-to-LDS loads (one 1 KiB token row
-  // per wave instruction, four per wave)
-  auto issue_raw = [&](int sb) {
+  // q for the B pieces: lane (n, qd) = (lane / 4, lane % 4) of wave w builds
+  // token n's pieces of slot qd for groups w and w + 4 (item k = 0, 1).  It
+  // reads the 20 bytes of code dword qd's partners (X) and those of code
+  // dword qd + 4 (Y, qd < 2) or the group's last 20 bytes (qd >= 2: bytes
+  // 120 .. 127 are the leftover dword's partners; qd = 3 uses none of it).
+  // Groups past G and tokens past the end read valid bytes that no stored
+  // output uses.
+  const int bn = lane >> 2, bq = lane & 3;
+  const int bx = 20 * bq, by = bq < 2 ? 20 * (bq + 4) : 108;
+  uint32_t qx[2][5], qy[2][5];
+  auto load_q = [&](int sb) {
+    const size_t t = (size_t)min(tok0 + bn, tokens - 1);
 #pragma unroll
-    for (int i = 0; i < kTok / 4; ++i) {
-      const int n = wave * (kTok / 4) + i;
-      const size_t t = (size_t)min(tok0 + n, tokens - 1);
-      const size_t off = min((size_t)sb * 1024 + (size_t)lane * 16, K - 16);  // groups past G: any bytes of the row
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(q + t * K + off),
-                                       (__attribute__((address_space(3))) void*)&st.raw[n][0], 16, 0, 0);
+    for (int k = 0; k < 2; ++k) {
+      const int g = min(sb * 8 + wave + 4 * k, G - 1);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(q + t * K + (size_t)g * 128);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        qx[k][i] = src[bx / 4 + i];
+        qy[k][i] = src[by / 4 + i];
+      }
     }
   };
   // scales (threads 0..63: one row's 8 fp16), partial sums (threads 0..127:
@@ -159,50 +162,46 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
       st.qs[tid & 7][tid >> 3] = s;
     }
   };
-  // B pieces from the q copy: task i = (token n, group g, c): c < 6 is code
-  // dword c of the group (20 bytes of q -> 5 trit dwords of lane c % 4, as
-  // X if c < 4, else as Y), c = 6 the leftover dword (Y of lane 2: the
-  // group's bytes 24, 25 in its half, zeros elsewhere)
+  // B pieces from the q registers.  Trit dword j of a code dword is partnered
+  // by its bytes' activations 5 apart: from 20 bytes w (5 dwords) entry e[j]
+  // holds bytes j, 5 + j, 10 + j, 15 + j (two byte permutes of two dwords
+  // each, merged).  Pieces of slot qd: [X0..X3], [X4, Y0..Y2], [Y3, Y4, 0, 0]
+  // with X = code dword qd's entries and Y = code dword qd + 4's (qd < 2),
+  // the leftover dword's (qd = 2: the group's bytes 24, 25 in its half of the
+  // dword -- low half for an even group -- and zeros in the other half, the
+  // padding trits of byte 25 meeting zeros) or zeros (qd = 3).
+  auto entries = [](const uint32_t* w, uint32_t* e) __attribute__((always_inline)) {
+    e[0] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0500u) | __builtin_amdgcn_perm(w[3], w[2], 0x07020C0Cu);
+    e[1] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0601u) | __builtin_amdgcn_perm(w[4], w[2], 0x04030C0Cu);
+    e[2] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0702u) | __builtin_amdgcn_perm(w[4], w[3], 0x05000C0Cu);
+    e[3] = __builtin_amdgcn_perm(w[2], w[0], 0x0C0C0403u) | __builtin_amdgcn_perm(w[4], w[3], 0x06010C0Cu);
+    e[4] = __builtin_amdgcn_perm(w[2], w[1], 0x0C0C0500u) | __builtin_amdgcn_perm(w[4], w[3], 0x07020C0Cu);
+  };
   auto build_b = [&]() {
-    auto byte = [](uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; };
-#pragma unroll 1
-    for (int i = tid; i < kTok * 8 * 7; i += 256) {
-      const int c = i % 7, rest = i / 7;
-      const int g = rest & 7, n = rest >> 3;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(&st.raw[n][0]) + g * 32;
-      uint32_t e[5];
-      int lq, u0;
-      if (c < 6) {
-        uint32_t w[5];
 #pragma unroll
-        for (int k = 0; k < 5; ++k) w[k] = src[5 * c + k];
-        // e[j] = bytes j, 5 + j, 10 + j, 15 + j of the 20: two byte permutes
-        // of two dwords each, merged
-        e[0] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0500u) | __builtin_amdgcn_perm(w[3], w[2], 0x07020C0Cu);
-        e[1] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0601u) | __builtin_amdgcn_perm(w[4], w[2], 0x04030C0Cu);
-        e[2] = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0702u) | __builtin_amdgcn_perm(w[4], w[3], 0x05000C0Cu);
-        e[3] = __builtin_amdgcn_perm(w[2], w[0], 0x0C0C0403u) | __builtin_amdgcn_perm(w[4], w[3], 0x06010C0Cu);
-        e[4] = __builtin_amdgcn_perm(w[2], w[1], 0x0C0C0500u) | __builtin_amdgcn_perm(w[4], w[3], 0x07020C0Cu);
-        lq = c & 3;
-        u0 = c < 4 ? 0 : 5;
-      } else {
-        const uint32_t u_lo = src[30], u_hi = src[31];  // q[120 .. 123], q[124 .. 127]
+    for (int k = 0; k < 2; ++k) {
+      const int g = wave + 4 * k;
+      uint32_t ex[5], ey[5];
+      entries(qx[k], ex);
+      if (bq < 2) {
+        entries(qy[k], ey);
+      } else if (bq == 2) {
+        // bytes 120 .. 123 and 124 .. 127 of the group are qy[k][3], qy[k][4]
+        const uint32_t u_lo = qy[k][3], u_hi = qy[k][4];
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
-          const uint32_t a = j < 4 ? byte(u_lo, j) : byte(u_hi, 0);  // q[120 + j]: byte 24
-          const uint32_t b = j < 3 ? byte(u_hi, j + 1) : 0u;         // q[125 + j]: byte 25 (3, 4 are padding)
+          const uint32_t a = j < 4 ? (u_lo >> (8 * j)) & 0xffu : u_hi & 0xffu;  // q[120 + j]: byte 24
+          const uint32_t b = j < 3 ? (u_hi >> (8 * (j + 1))) & 0xffu : 0u;      // q[125 + j]: byte 25
           const uint32_t lo = a | (b << 8);
-          e[j] = (g & 1) ? lo << 16 : lo;
+          ey[j] = (g & 1) ? lo << 16 : lo;
         }
-        lq = 2;
-        u0 = 5;
-      }
-      uint32_t* img = reinterpret_cast<uint32_t*>(&st.bimg[g][0][n][lq]);  // + s * kTok * 16 + pos
+      } else {
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {
-        const int u = u0 + j;
-        img[(u >> 2) * kTok * 16 + (u & 3)] = e[j];
+        for (int j = 0; j < 5; ++j) ey[j] = 0u;
       }
+      st.bimg[g][0][bn][bq] = v4u{ex[0], ex[1], ex[2], ex[3]};
+      st.bimg[g][1][bn][bq] = v4u{ex[4], ey[0], ey[1], ey[2]};
+      st.bimg[g][2][bn][bq] = v4u{ey[3], ey[4], 0u, 0u};
     }
   };
 
@@ -228,11 +227,11 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
   };
 
   double total[4] = {0.0, 0.0, 0.0, 0.0};
-  issue_raw(0);
+  load_q(0);
   load_side(0);
   load_codes(0);
   for (int sb = 0; sb < G8; ++sb) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the q copy (and everything else) has landed
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this superblock's q, codes and side inputs have landed
     __syncthreads();                          // ... for every wave; the last superblock's reads are done
     store_side();
     build_b();
@@ -240,7 +239,7 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 16; ++k) cdw[k] = cdn[k];
     const int sbn = min(sb + 1, G8 - 1);  // the last superblock re-reads itself: no branch, exact waits
-    issue_raw(sbn);
+    load_q(sbn);
     load_side(sbn);
     load_codes(sbn);
 
@@ -290,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm_ptq1_kernel(const v4u* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) total[i] = sb == 0 ? acc[i] : total[i] + acc[i];
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no copy into LDS outstanding at exit
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no load outstanding at exit
   if (IDOTS) return;
   const int tk = tok0 + r;
   if (tk >= tokens) return;
