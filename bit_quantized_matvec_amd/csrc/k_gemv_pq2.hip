@@ -327,21 +327,38 @@ __global__ __launch_bounds__(64 * kMaxWaves, 2) void gemv_pq2_batch_kernel(GemvB
 
 GemvPlan plan_gemv_pq2(const Dims& dm, bool have_workspace) {
   // Measured on MI355X: with 384 or more row tiles one workgroup per tile is
-  // fastest (the extra workgroups of a split only add reduction work).  With
-  // fewer tiles, the columns are split into the fewest slices that keep each
-  // of 4 waves to a run of at most 3 superchunks and give at least 224
-  // workgroups, keeping at least 4 superchunks per slice (a split of a tiny
-  // row only adds the reduction: 256 x 1024 takes 2.9 us unsplit, 4.2 split).  Fused kernel, best
-  // split of a sweep vs this rule: 5120 x 6144 3 slices 5.97 us (rule: same;
-  // the earlier ~384-workgroup rule: 7.5 us), 7168 x 5120 2 slices 6.79 us
-  // (same; 7.25), 5120 x 17408 6 slices 10.42 us (same; 10.71), 17408 x 5120
-  // 3 slices 10.09 us (rule 2 slices: 10.65).
+  // fastest (32768 x 8192: 13.7 us; split in 2 or 4 slices: 15.4, 17.1).
+  // With fewer tiles the columns are split.  Of the slice counts that give
+  // each wave a run of 2 or 3 superchunks (at least 4 superchunks per
+  // slice), the one with the least work on the busiest compute unit --
+  // ceil(workgroups / 256) x superchunks per slice -- is taken, ties going to
+  // more slices; without such a count, runs of any length from 2.  Fused
+  // kernel, us per slice count 2 / 3 / 4 / 5 / 6 / 9 / 12 (rule's pick *):
+  // 17408 x 5120 9.60 / 8.99 / 8.93* / 9.75 / 9.75 / 9.61 / 9.54; 7168 x
+  // 5120 6.58 / 6.56 / 5.93* / 6.43 / 6.43 / 6.34 / 6.17; 5120 x 6144 6.45 /
+  // 5.24* / 6.15 / 5.91 / 5.37 / 6.02 / 5.49; 5120 x 17408 12.70 / 9.21 /
+  // 11.11 / 9.01 / 8.17 / 8.10 / 8.09*.  A tiny row is not split (256 x
+  // 1024 takes 2.9 us unsplit, 4.2 split).
   GemvPlan p;
   const int nsc = (int)dm.nsc;
   int slices = 1;
   if (have_workspace && dm.ntiles < 384) {
     const int most_slices = std::min(kMaxSlices, std::max(1, nsc / 4));
-    while (slices < most_slices && ((nsc + slices - 1) / slices > kPlanWaves * 3 || dm.ntiles * slices < 224)) ++slices;
+    for (int pass = 0; pass < 2 && slices == 1; ++pass) {
+      const int longest = pass == 0 ? 3 : nsc;  // runs of 2 or 3 superchunks, else of any length from 2
+      int64_t best_cost = -1;
+      for (int sl = 2; sl <= most_slices; ++sl) {
+        const int scw = (nsc + sl - 1) / sl;
+        const int w = std::min(scw, kPlanWaves);
+        const int run = (scw + w - 1) / w;
+        if (run < 2 || run > longest) continue;
+        const int64_t cost = (dm.ntiles * sl + 255) / 256 * scw;
+        if (best_cost < 0 || cost <= best_cost) {
+          best_cost = cost;
+          slices = sl;
+        }
+      }
+    }
   }
   p.scw = (nsc + slices - 1) / slices;
   p.slices = (nsc + p.scw - 1) / p.scw;
