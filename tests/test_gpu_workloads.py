@@ -78,3 +78,32 @@ def test_gate_up_batch_launch(tq, orc):
     per = tq.workspace_bytes("pq2_0", 64, 256)
     idx = torch.arange(pair_rows // 64, device="cuda") * per
     assert int(torch.count_nonzero(torch.stack([ws[idx + k] for k in range(4)]))) == 0
+
+
+@pytest.mark.parametrize("R,K", [(5120, 17408), (7168, 5120), (5120, 6144)])
+def test_step_launches_with_workspace(tq, orc, R, K):
+    """The 64-layer step's other launches (down 5120 x 17408, qkv 7168 x 5120,
+    out 5120 x 6144): tq_gemv_f32 with a workspace, which splits the columns
+    of these matrices (fewer than 384 row tiles), twice in a row, against
+    tq_quantize_q8k + tq_gemv with the same workspace (bit-identical) and the
+    oracle on sampled rows; the arrival counters are back at zero."""
+    from test_gpu_parity import counters_clear
+
+    g = TI.rng(TI.STEP64, 1, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    x = TI.activations(g, 1, K)
+    say("step launch with workspace", R, K)
+    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    ws = tq.workspace("pq2_0", R, K)
+    xd = dev(x[0])
+    y1 = host(tq.gemv_f32("pq2_0", Wd, R, K, xd, ws=ws))
+    assert counters_clear(tq, ws, -(-R // 64))
+    y2 = host(tq.gemv_f32("pq2_0", Wd, R, K, xd, ws=ws))
+    q, d, _ = tq.quantize_q8k(dev(x))
+    yq = host(tq.gemv("pq2_0", Wd, R, K, q, d, ws=ws))
+    assert np.array_equal(y1, y2) and np.array_equal(y1, yq)
+    assert counters_clear(tq, ws, -(-R // 64))
+    rows = sample_rows(R, 60)
+    qo, do, _ = orc.quantize_q8k(x)
+    yo, mag = orc.matmul_rows("pq2_0", W, qo, do, rows, with_mag=True)
+    assert_close_rows(y1[rows], yo[0], mag[0], what=f"step launch {R}x{K}")
