@@ -107,3 +107,23 @@ def test_step_launches_with_workspace(tq, orc, R, K):
     qo, do, _ = orc.quantize_q8k(x)
     yo, mag = orc.matmul_rows("pq2_0", W, qo, do, rows, with_mag=True)
     assert_close_rows(y1[rows], yo[0], mag[0], what=f"step launch {R}x{K}")
+
+
+@pytest.mark.parametrize("R,K", [(28672, 3072), (28672, 2048)])
+def test_gemv_f32_full_grid_one_slot(tq, orc, R, K):
+    """A full grid (448 row tiles) with runs of 3 and 2 superchunks: the fused
+    product keeps one ring slot there and quantizes its run in batches of 4
+    and 2 blocks.  Bit-identical to tq_quantize_q8k + tq_gemv, and the oracle
+    on sampled rows."""
+    g = TI.rng(77, 41, R, K)
+    W = TI.pq2_matrix(g, R, K)
+    x = TI.activations(g, 1, K)
+    say("full grid, one ring slot", R, K)
+    Wd = tq.repack(dev(W.reshape(-1)), "pq2_0", R, K)
+    y = host(tq.gemv_f32("pq2_0", Wd, R, K, dev(x[0])))
+    q, d, _ = tq.quantize_q8k(dev(x))
+    assert np.array_equal(y, host(tq.gemv("pq2_0", Wd, R, K, q, d)))
+    rows = sample_rows(R, 61)
+    qo, do, _ = orc.quantize_q8k(x)
+    yo, mag = orc.matmul_rows("pq2_0", W, qo, do, rows, with_mag=True)
+    assert_close_rows(y[rows], yo[0], mag[0], what=f"full grid {R}x{K}")
