@@ -375,18 +375,22 @@ def probe_lib():
     lib.tqp_read.restype = I
     lib.tqp_clock.argtypes = [P, I, I, P, I64, P]
     lib.tqp_clock.restype = I
+    lib.tqp_read_units.argtypes = [P, I, I, P, P]
+    lib.tqp_read_units.restype = I
     return lib
 
 
 READ_BLOCKS, READ_THREADS = 8192, 512  # the fastest shape of a sweep of the read kernel
+DECODE_TILES, DECODE_UNITS = 512, 32  # 32768 x 8192: row tiles of 64, units of 256 columns
 
 
 def ceiling_bench(torch, bufs, K, trials):
     """Streaming reads with libtq_probe's read kernel: one pass over each of the
     rotated 71 MB weight copies (the decode step's own buffers, so the same
-    one-shot, cache-cold traffic), and over a 1 GiB buffer; plus the shader
-    clock (s_memtime against the 100 MHz s_memrealtime), idle and while
-    streaming."""
+    one-shot, cache-cold traffic), and over a 1 GiB buffer; the same copies
+    read with the decode product's own pattern (its grid, waves, units and
+    two-unit ring, no arithmetic); plus the shader clock (s_memtime against
+    the 100 MHz s_memrealtime), idle and while streaming."""
     import ctypes
 
     lib = probe_lib()
@@ -404,6 +408,17 @@ def ceiling_bench(torch, bufs, K, trials):
         read(bufs[i % len(bufs)])
     r71 = per_call_us(graph_trials(torch, lambda i: read(bufs[i % len(bufs)]), K, trials), K)
     r71_c = per_call_us(graph_trials(torch, lambda i: read(bufs[i % len(bufs)], 0), K, trials), K)
+
+    def read_units(buf):
+        # the decode's 512 row tiles of 32 units (4352 bytes each)
+        st = lib.tqp_read_units(ctypes.c_void_p(buf.data_ptr()), DECODE_TILES, DECODE_UNITS,
+                                ctypes.c_void_p(sink.data_ptr()), stream())
+        if st != 0:
+            raise RuntimeError(f"tqp_read_units failed: hipError {st}")
+
+    if nb != DECODE_TILES * DECODE_UNITS * 4352:
+        raise RuntimeError("the rotated copies are not the decode's 512 x 32 units")
+    r71_p = per_call_us(graph_trials(torch, lambda i: read_units(bufs[i % len(bufs)]), K, trials), K)
     big = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
     for _ in range(3):
         read(big)
@@ -425,6 +440,7 @@ def ceiling_bench(torch, bufs, K, trials):
     del big
     return {"read_71MB_rotated_us": r71["us"], "read_71MB_rotated_gbs": nb / r71["us"] / 1e3,
             "read_71MB_rotated_cached_loads_gbs": nb / r71_c["us"] / 1e3,
+            "read_71MB_decode_pattern_us": r71_p["us"], "read_71MB_decode_pattern_gbs": nb / r71_p["us"] / 1e3,
             "read_1GiB_gbs": (1 << 30) / rbig["us"] / 1e3,
             "read_shape": f"{READ_BLOCKS} workgroups x {READ_THREADS} threads, 4 x 16 B non-temporal loads in flight per thread",
             "sclk_mhz_spin": mhz["spin"], "sclk_mhz_streaming": mhz["streaming"]}
@@ -500,6 +516,9 @@ def probe_workloads(torch, tq, names):
             for i in range(n):
                 lib.tqp_read(ctypes.c_void_p(Ws[i % len(Ws)].data_ptr()), Ws[0].numel(), READ_BLOCKS, READ_THREADS, 1,
                              ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            for i in range(n):
+                lib.tqp_read_units(ctypes.c_void_p(Ws[i % len(Ws)].data_ptr()), DECODE_TILES, DECODE_UNITS,
+                                   ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         del Ws
     if every or "quant" in names:
@@ -642,7 +661,7 @@ def summarize(counter_dir, trace_dir=None):
     out = {}
     for key in sorted(set(med) | set(durations), key=lambda k: (k[0], k[1])):
         fam = kernel_family(key[0])
-        if fam is None and "copyBuffer" not in key[0] and "read_kernel" not in key[0]:
+        if fam is None and "copyBuffer" not in key[0] and "read_kernel" not in key[0] and "units_kernel" not in key[0]:
             continue
         cs = med.get(key, {})
         e = {"kernel": key[0], "grid": key[1], "block": key[2], "lds": lds.get(key), "family": fam}

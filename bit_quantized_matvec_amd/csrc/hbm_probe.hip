@@ -7,6 +7,12 @@
 //     compared with, in the spirit of the pages' first measurement (page 1,
 //     "the ceiling": a plain loop summing a large buffer before any kernel
 //     work);
+//   * the decode product's own read pattern without its arithmetic: one
+//     workgroup of four waves per 64-row tile of 4352-byte units (4 KiB of
+//     codes as four 1 KiB wave loads, then 256 bytes of scale pairs, one
+//     dword per lane), each wave streaming its run of units with two in
+//     flight, XOR-folded; it separates what the access pattern costs from
+//     what the product's work between fetches costs;
 //   * a shader-clock probe: s_memtime (core clock) against s_memrealtime
 //     (fixed 100 MHz) over a spin loop, optionally while streaming a buffer,
 //     so that a run records the clock its figures were taken at.
@@ -34,6 +40,38 @@ __global__ __launch_bounds__(512) void read_kernel(const v4u* __restrict__ p, in
   }
   for (; i < n; i += stride) acc ^= ld<NT>(p + i);
   const unsigned r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == 0x9e3779b9u) sink[0] = r;  // practically never taken; keeps the loads alive
+}
+
+constexpr int kUnitBytes = 4352;  // one pq2_0 unit: 64 rows x 256 columns of codes, then 64 scale pairs
+
+__global__ __launch_bounds__(256) void units_kernel(const uint8_t* __restrict__ w, int units_per_tile, int upw,
+                                                    unsigned* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint8_t* tile = w + (size_t)blockIdx.x * units_per_tile * kUnitBytes;
+  const int u0 = wave * upw;
+  v4u rc[2][4];
+  unsigned rs[2];
+  v4u acc = {0u, 0u, 0u, 0u};
+  unsigned accs = 0;
+  // unit k of the run into slot j (past the run: its last unit again, so every load stays in bounds)
+  auto fetch = [&](int j, int k) __attribute__((always_inline)) {
+    const uint8_t* p = tile + (size_t)(u0 + min(k, upw - 1)) * kUnitBytes;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) rc[j][qd] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + qd * 1024) + lane);
+    rs[j] = reinterpret_cast<const unsigned*>(p + 4096)[lane];
+  };
+  fetch(0, 0);
+  fetch(1, 1);
+  for (int k = 0; k < upw; k += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc ^= rc[j][0] ^ rc[j][1] ^ rc[j][2] ^ rc[j][3];
+      accs ^= rs[j];
+      fetch(j, k + j + 2);
+    }
+  }
+  const unsigned r = acc.x ^ acc.y ^ acc.z ^ acc.w ^ accs;
   if (r == 0x9e3779b9u) sink[0] = r;  // practically never taken; keeps the loads alive
 }
 
@@ -75,6 +113,18 @@ int tqp_read(const void* buf, int64_t bytes, int blocks, int threads, int nontem
     hipLaunchKernelGGL(read_kernel<true>, dim3(blocks), dim3(threads), 0, s, p, bytes / 16, sink);
   else
     hipLaunchKernelGGL(read_kernel<false>, dim3(blocks), dim3(threads), 0, s, p, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// The decode product's read pattern over `tiles` row tiles of `units_per_tile`
+// 4352-byte units each (tiles * units_per_tile * 4352 bytes of 16-byte
+// aligned device memory), four waves per tile, each wave a run of
+// units_per_tile / 4 units (units_per_tile a positive multiple of 8).
+// sink: one device uint32.  Returns 0 or a hipError_t.
+int tqp_read_units(const void* buf, int tiles, int units_per_tile, unsigned* sink, void* stream) {
+  if (!buf || !sink || tiles < 1 || units_per_tile < 8 || units_per_tile % 8) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(units_kernel, dim3(tiles), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(buf), units_per_tile, units_per_tile / 4, sink);
   return (int)hipGetLastError();
 }
 
