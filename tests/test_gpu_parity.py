@@ -310,7 +310,9 @@ def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
     pair's inner sum once and sum the superchunks in the same runs and run
     order; the column counts give runs of 1, 2, 2, 4 and 5 superchunks with
     ragged last runs, and the token counts every result-slot layout of the
-    one-block kernel (1-4, 5-8 and 9-16 tokens) and the two-block one.  ptq1_0: every token of a block takes the one-token
+    one-block kernel (1-4, 5-8 and 9-16 tokens), two and three 16-token
+    groups (17, 40) and one and two 32-token groups (50, 64), the last group
+    part empty.  ptq1_0: every token of a block takes the one-token
     kernel's steps (blocks of 1, 2 or 4 tokens, the last one padded).
     A workspace changes nothing (twice in a row, arrival counters at zero).
     17408x5120 is the prefill shape."""
@@ -319,7 +321,7 @@ def test_gemm_equals_stacked_gemv(tq, fmt, R, K):
     g = TI.rng(77, 15, R, K)
     W = TI.pq2_matrix(g, R, K) if fmt == "pq2_0" else TI.ptq1_matrix(g, R, K)
     Wd = tq.repack(dev(W.reshape(-1)), fmt, R, K)
-    for T in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 64):
+    for T in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 40, 50, 64):
         say("gemm vs gemv", fmt, R, K, T)
         x = TI.activations(g, T, K)
         q, d, bs = tq.quantize_q8k(dev(x))
