@@ -12,7 +12,8 @@
 //   * per superchunk a lane issues four non-temporal dwordx4 loads (qd = 0..3),
 //     each a fully coalesced 1 KiB wave request (the codes are never reused),
 //     plus its row's scale pair from the 256 bytes that follow the codes in
-//     the same 4352-byte unit, two superchunks ahead of their use;
+//     the same 4352-byte unit, one or two superchunks ahead of their use
+//     (the ring's depth: two, or one for short runs on a full grid);
 //   * the activation bytes a lane needs are the same for every lane of the
 //     wave: the workgroup stages its slice of them in LDS once, and each
 //     superchunk's 256 bytes are read from there with broadcast 16-byte
