@@ -180,3 +180,25 @@ def test_no_cpu_fallback_in_binding():
     assert "oracle" not in src.replace("no CPU fallback", "")
     for f in os.listdir(os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "bit_quantized_matvec_amd", "csrc", f)).read().lower()
+
+
+def test_probe_library_validates_on_host(tq):
+    """The measurement library beside the product (libtq_probe.so: the read
+    ceiling, the decode-pattern read and the clock) loads and refuses bad
+    arguments before any HIP work (hipErrorInvalidValue = 1)."""
+    path = os.path.join(ROOT, "bit_quantized_matvec_amd", "libtq_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libtq_probe.so is not built")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.tqp_read.argtypes = [P, I64, I, I, I, P, P]
+    lib.tqp_read_units.argtypes = [P, I, I, P, P]
+    lib.tqp_clock.argtypes = [P, I, I, P, I64, P]
+    fake = ctypes.c_void_p(16)
+    assert lib.tqp_read(None, 1024, 8, 64, 1, fake, None) == 1
+    assert lib.tqp_read(fake, 1000, 8, 64, 1, fake, None) == 1  # not a multiple of 16
+    assert lib.tqp_read(fake, 1024, 8, 48, 1, fake, None) == 1  # threads not a multiple of 64
+    assert lib.tqp_read_units(None, 512, 32, fake, None) == 1
+    assert lib.tqp_read_units(fake, 512, 12, fake, None) == 1   # runs of 3: not a multiple of 8 units
+    assert lib.tqp_read_units(fake, 0, 32, fake, None) == 1
+    assert lib.tqp_clock(None, 8, 10, None, 0, None) == 1
